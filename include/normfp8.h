@@ -1,0 +1,191 @@
+/*
+ * normfp8.h -- C ABI of the fused LayerNorm / RMSNorm + FP8 library for AMD MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [XLA-Norm]  "Implementation: NVIDIA TransformerEngine JAX XLA Normalization"
+ *   [BwdAdd]    "Implementation: NVIDIA TransformerEngine Ops Fused Backward Add RMSNorm"
+ *   [NVRTC-PR]  "Migrate norms and softmax kernels to NVRTC" (TransformerEngine pull request)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All functions are extern "C", thread-safe and non-blocking. They return NORM_OK (0) or
+ *    a norm_status_t; norm_last_error() gives a message for the calling thread.
+ *  - Arguments are validated on the host before anything is enqueued: on any error nothing
+ *    has been enqueued on the stream.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream. Work is
+ *    enqueued on that stream only. The library never synchronises, never allocates or frees
+ *    device memory and never reads device memory on the host (norm_workspace_check excepted).
+ *  - Tensors are device pointers to dense row-major storage. x-like tensors are [rows, hidden]
+ *    with row stride `hidden`. Pointers must be 16-byte aligned; `hidden` must be a multiple
+ *    of 8. The caller owns every buffer, including the workspace.
+ *  - Element types are given by norm_dtype_t codes. Statistics (mu, rsigma) and the amax /
+ *    scale / scale_inv scalars are always float32. rows == 0 is valid: row-indexed buffers
+ *    (x, y, y_colwise, dy, dx, residual_dy, mu, rsigma, MXFP8 scale grids) may then be NULL;
+ *    delayed scaling still writes updated_amax = *amax and scale_inv, and the backward
+ *    writes zero weight gradients.
+ *  - Workspace: the size comes from the *_workspace_size query for the same arguments. Every
+ *    workspace begins with a NORM_WS_HEADER_BYTES synchronisation header that must be all
+ *    zero before the workspace is first used (zero-fill it, or call norm_workspace_init once).
+ *    Every call leaves the header zeroed again, so one workspace can serve any sequence of
+ *    calls, of any shape, issued in order on one stream. Two calls that may run at the same
+ *    time (different streams) must not share a workspace.
+ */
+#ifndef NORMFP8_H
+#define NORMFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NORMFP8_ABI_VERSION 1
+#define NORM_WS_HEADER_BYTES 16384
+
+typedef enum {
+  NORM_OK = 0,
+  NORM_ERR_INVALID_ARG = 1,         /* NULL where a pointer is required, bad enum, negative size */
+  NORM_ERR_UNSUPPORTED = 2,         /* valid request outside what this build implements */
+  NORM_ERR_MISALIGNED = 3,          /* pointer not 16-byte aligned */
+  NORM_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes below the query's answer */
+  NORM_ERR_HIP = 5                  /* a HIP runtime call failed (message has hipGetErrorString) */
+} norm_status_t;
+
+/* [XLA-Norm] Signature, I/O Contract: the norm type input selects LayerNorm or RMSNorm. */
+typedef enum { NORM_LAYERNORM = 0, NORM_RMSNORM = 1 } norm_type_t;
+
+/* [XLA-Norm] Signature: separate input, weight and output element types. */
+typedef enum {
+  NORM_F32 = 0,
+  NORM_F16 = 1,
+  NORM_BF16 = 2,
+  NORM_FP8_E4M3 = 3, /* OCP E4M3 ("FN": bias 7, no inf, max 448) */
+  NORM_FP8_E5M2 = 4  /* OCP E5M2 (bias 15, IEEE-style inf/NaN, max 57344) */
+} norm_dtype_t;
+
+/* [XLA-Norm] Description: delayed per-tensor scaling, MXFP8 block scaling, or no scaling. */
+typedef enum {
+  NORM_SCALING_NONE = 0,
+  NORM_SCALING_DELAYED_TENSOR = 1,
+  NORM_SCALING_MXFP8_1D32 = 2 /* 32-element blocks, one E8M0 scale byte per block */
+} norm_scaling_t;
+
+/* [XLA-Norm] Signature / Description: rowwise output with optional columnwise output. */
+typedef enum {
+  NORM_Q_ROWWISE = 1,
+  NORM_Q_COLWISE = 2,
+  NORM_Q_ROWWISE_COLWISE = 3
+} norm_qlayout_t;
+
+/*
+ * norm_fwd_workspace_size -- bytes of workspace norm_fwd needs for these arguments.
+ * [XLA-Norm] Description, Signature (forward workspace query: batch, hidden, the three element
+ * types, norm type, scaling mode, zero-centred gamma, epsilon, SM margin, training flag).
+ * `cu_margin` is the number of compute units the launch plan leaves free, as the pages' SM
+ * margin. The answer depends only on the arguments (not on the device), so it can be taken
+ * without a GPU. *bytes == 0 means workspace may be NULL.
+ */
+int norm_fwd_workspace_size(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype,
+                            int norm_type, int scaling, int qlayout, int zero_centered_gamma,
+                            float epsilon, int cu_margin, int is_training, size_t *bytes);
+
+/*
+ * norm_bwd_workspace_size -- bytes of workspace norm_bwd / norm_bwd_add need.
+ * [XLA-Norm] Signature (backward workspace query); [NVRTC-PR] Flowchart (the backward keeps
+ * per-workgroup weight-gradient partials for a finalize step). `with_add` selects norm_bwd_add.
+ */
+int norm_bwd_workspace_size(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_type,
+                            int zero_centered_gamma, float epsilon, int cu_margin, int with_add,
+                            size_t *bytes);
+
+/*
+ * norm_fwd -- normalise each row of x and store the output, optionally FP8-quantised, in one
+ * kernel launch. [XLA-Norm] Overview, Description, Signature (NormForwardFFI argument list),
+ * I/O Contract.
+ *
+ *   x [rows, hidden] in_dtype; gamma [hidden] w_dtype; beta [hidden] w_dtype (LayerNorm only,
+ *   must be NULL for RMSNorm).
+ *   Statistics: mu [rows] (LayerNorm; NULL allowed) = row mean; rsigma [rows] (NULL allowed)
+ *   = 1/sqrt(biased variance + epsilon) for LayerNorm, 1/sqrt(mean(x^2) + epsilon) for RMSNorm.
+ *   Effective weight g = gamma, or 1 + gamma when zero_centered_gamma != 0.
+ *   y_row = (x - mu) * rsigma * g + beta (LayerNorm) or x * rsigma * g (RMSNorm), in float32.
+ *
+ *   scaling == NORM_SCALING_NONE: y [rows, hidden] out_dtype (F32/F16/BF16), round-to-nearest-
+ *     even of y_row. y_colwise, scale, amax, scale_inv, colwise_scale_inv, updated_amax unused
+ *     (pass NULL). qlayout must be NORM_Q_ROWWISE.
+ *   scaling == NORM_SCALING_DELAYED_TENSOR: out_dtype FP8_E4M3 or FP8_E5M2; scale, amax: device
+ *     float32[1] inputs; codes = saturating nearest-even FP8 of y_row * scale. Rowwise codes in y
+ *     [rows, hidden]; columnwise codes in y_colwise [hidden, rows] (the transpose). scale_inv and
+ *     colwise_scale_inv (float32[1] each, for the layouts requested) receive 1/scale.
+ *     updated_amax (float32[1], may alias amax) receives max(*amax, max |y_row|) over the tensor.
+ *   scaling == NORM_SCALING_MXFP8_1D32: out_dtype FP8_E4M3 or FP8_E5M2; each block of 32
+ *     consecutive elements (along a row for rowwise, along a column for columnwise; a final
+ *     shorter block where the dimension is not a multiple of 32) shares the E8M0 scale
+ *     2^X, X = clamp(floor(log2 amax_block) - emax, -127, 127) (emax 8 for E4M3, 15 for E5M2;
+ *     X = -127 for an all-zero block); codes = saturating nearest-even FP8 of y_row * 2^-X.
+ *     Rowwise: y [rows, hidden] codes, scale_inv = uint8 [rows, ceil(hidden/32)] bytes X+127.
+ *     Columnwise: y_colwise [hidden, rows] codes, colwise_scale_inv = uint8
+ *     [hidden, ceil(rows/32)]. scale, amax, updated_amax unused (NULL).
+ *   The layout pointers not requested by qlayout must be NULL.
+ *
+ *   Errors: NORM_ERR_INVALID_ARG for NULL required pointers or bad codes; NORM_ERR_UNSUPPORTED
+ *   for a dtype / layout combination this build does not implement; NORM_ERR_MISALIGNED;
+ *   NORM_ERR_WORKSPACE_TOO_SMALL; NORM_ERR_HIP if the launch fails.
+ */
+int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, const float *scale,
+             const float *amax, void *y, void *y_colwise, float *mu, float *rsigma, void *scale_inv,
+             void *colwise_scale_inv, float *updated_amax, void *workspace, size_t workspace_bytes,
+             int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
+             int scaling, int qlayout, int zero_centered_gamma, float epsilon, int cu_margin);
+
+/*
+ * norm_bwd -- LayerNorm / RMSNorm backward. [XLA-Norm] Description (backward dispatch);
+ * [NVRTC-PR] Flowchart and file table (partial weight-gradient kernel, then a finalize kernel).
+ *
+ *   dy, x [rows, hidden] in_dtype; mu [rows] float32 (LayerNorm; NULL for RMSNorm);
+ *   rsigma [rows] float32 (the forward's outputs); gamma [hidden] w_dtype.
+ *   xhat = (x - mu) * rsigma (LayerNorm) or x * rsigma (RMSNorm); w = dy * g.
+ *   dx = rsigma * (w - mean(w) - xhat * mean(w * xhat))  (LayerNorm),
+ *   dx = rsigma * (w - xhat * mean(w * xhat))            (RMSNorm), stored in in_dtype.
+ *   dgamma [hidden] w_dtype = sum over rows of dy * xhat; dbeta [hidden] w_dtype = sum of dy
+ *   (LayerNorm only; NULL for RMSNorm). The row sums are reduced in a fixed order, so repeated
+ *   calls give bitwise-identical results.
+ */
+int norm_bwd(void *stream, const void *dy, const void *x, const float *mu, const float *rsigma,
+             const void *gamma, void *dx, void *dgamma, void *dbeta, void *workspace,
+             size_t workspace_bytes, int64_t rows, int64_t hidden, int in_dtype, int w_dtype,
+             int norm_type, int zero_centered_gamma, int cu_margin);
+
+/*
+ * norm_bwd_add -- fused RMSNorm backward plus residual gradient. [BwdAdd] Overview,
+ * Description, I/O Contract: one kernel produces dx = rmsnorm_dx + residual_dy (summed in
+ * float32, rounded once) and the weight gradient.
+ *   residual_dy [rows, hidden] in_dtype; other arguments as norm_bwd with norm type RMSNorm.
+ */
+int norm_bwd_add(void *stream, const void *dy, const void *x, const void *residual_dy,
+                 const float *rsigma, const void *gamma, void *dx, void *dgamma, void *workspace,
+                 size_t workspace_bytes, int64_t rows, int64_t hidden, int in_dtype, int w_dtype,
+                 int zero_centered_gamma, int cu_margin);
+
+/* Zero the synchronisation header of a new workspace (enqueues one small kernel on stream). */
+int norm_workspace_init(void *stream, void *workspace, size_t workspace_bytes);
+
+/*
+ * Diagnostic, blocking: synchronises `stream`, copies the header's error word to *flags
+ * (bit 0: a cross-workgroup wait exceeded its time limit; bit 1: header found corrupt) and
+ * clears it. Not for the hot path.
+ */
+int norm_workspace_check(void *stream, void *workspace, uint32_t *flags);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char *norm_last_error(void);
+
+/* NORMFP8_ABI_VERSION of the built library. */
+int norm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NORMFP8_H */

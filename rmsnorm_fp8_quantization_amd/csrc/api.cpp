@@ -1,0 +1,513 @@
+// api.cpp -- the C ABI declared in include/normfp8.h: argument validation, the launch planner
+// and the kernel launches.
+//
+// [XLA-Norm] = "Implementation: NVIDIA TransformerEngine JAX XLA Normalization";
+// [NVRTC-PR] = "Migrate norms and softmax kernels to NVRTC" (TransformerEngine pull request).
+// [XLA-Norm] Description: workspace-size queries for forward and backward, a forward entry that
+// takes the input / weight / scaling buffers and writes the outputs, and an SM margin removed
+// from the device's multiprocessor count when sizing the launch. [NVRTC-PR] Flowchart: grid
+// sizes come from occupancy, multi-CTA rows use a workspace and barrier, and the backward
+// launches a finalize kernel after the partial weight-gradient kernel.
+//
+// MI355X design: every kernel is compiled ahead of time for gfx950 (no runtime compilation);
+// the planner picks one of three forward layouts (wave / workgroup team per row, or band tiles
+// with a cross-workgroup statistics exchange) from the row length and the requested outputs,
+// and the backward's persistent grid from the CU count less the margin. The planner never
+// reads device memory and never allocates.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "../../include/normfp8.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+static_assert(NORM_WS_HEADER_BYTES == nf8::kWsHeaderBytes, "workspace header size mismatch");
+
+namespace {
+
+using namespace nf8;
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+int ok() {
+  g_err.clear();
+  return NORM_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool is_hp(int dt) { return dt == DT_F32 || dt == DT_F16 || dt == DT_BF16; }
+bool is_fp8(int dt) { return dt == DT_E4M3 || dt == DT_E5M2; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+// optional integer override from the environment (planner testing / tuning knob)
+int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+// ---------------------------------------------------------------- device facts (cached)
+struct DeviceInfo {
+  int cus = 0;
+};
+std::mutex g_mu;
+std::unordered_map<int, DeviceInfo> g_dev;
+std::unordered_map<const void *, int> g_occ;  // kernel -> max resident workgroups per CU
+
+int device_info(DeviceInfo *out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(NORM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_dev.find(dev);
+  if (it == g_dev.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(NORM_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    DeviceInfo d;
+    d.cus = prop.multiProcessorCount;
+    it = g_dev.emplace(dev, d).first;
+  }
+  *out = it->second;
+  return NORM_OK;
+}
+
+int occupancy(const void *fn, int threads, int *out) {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_occ.find(fn);
+    if (it != g_occ.end()) {
+      *out = it->second;
+      return NORM_OK;
+    }
+  }
+  int n = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0);
+  if (e != hipSuccess) return fail(NORM_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+  if (n < 1) n = 1;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_occ[fn] = n;
+  *out = n;
+  return NORM_OK;
+}
+
+int launch(const void *fn, dim3 grid, dim3 block, void *param, hipStream_t stream) {
+  void *args[] = {param};
+  hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
+  if (e != hipSuccess) return fail(NORM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return NORM_OK;
+}
+
+// ---------------------------------------------------------------- forward plan
+struct FwdPlan {
+  int mode = MODE_PLAIN;
+  bool rowwise = true, colwise = false;
+  bool band = false;
+  int cfg = 0;
+  int S = 1;
+  int64_t bands = 0;
+  size_t ws_bytes = 0;
+  size_t partial_off = 0;
+};
+
+int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
+             int scaling, int qlayout, int cu_margin, FwdPlan *pl) {
+  if (rows < 0 || hidden <= 0) return fail(NORM_ERR_INVALID_ARG, "rows must be >= 0 and hidden > 0");
+  if (norm_type != NORM_LAYERNORM && norm_type != NORM_RMSNORM)
+    return fail(NORM_ERR_INVALID_ARG, "unknown norm_type %d", norm_type);
+  if (!is_hp(in_dtype)) return fail(NORM_ERR_UNSUPPORTED, "input dtype %d not supported", in_dtype);
+  if (!is_hp(w_dtype)) return fail(NORM_ERR_UNSUPPORTED, "weight dtype %d not supported", w_dtype);
+  if (cu_margin < 0) return fail(NORM_ERR_INVALID_ARG, "cu_margin must be >= 0");
+  if (qlayout < NORM_Q_ROWWISE || qlayout > NORM_Q_ROWWISE_COLWISE)
+    return fail(NORM_ERR_INVALID_ARG, "unknown quantize layout %d", qlayout);
+  if (hidden % 8 != 0) return fail(NORM_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 8", (long long)hidden);
+  if (hidden > (int64_t)1 << 24) return fail(NORM_ERR_UNSUPPORTED, "hidden above 2^24 not supported");
+  switch (scaling) {
+    case NORM_SCALING_NONE:
+      if (!is_hp(out_dtype)) return fail(NORM_ERR_UNSUPPORTED, "no-scaling output must be F32/F16/BF16");
+      if (qlayout != NORM_Q_ROWWISE) return fail(NORM_ERR_UNSUPPORTED, "no-scaling output is rowwise only");
+      pl->mode = MODE_PLAIN;
+      break;
+    case NORM_SCALING_DELAYED_TENSOR:
+    case NORM_SCALING_MXFP8_1D32:
+      if (!is_fp8(out_dtype)) return fail(NORM_ERR_UNSUPPORTED, "scaled output must be FP8_E4M3 or FP8_E5M2");
+      pl->mode = scaling == NORM_SCALING_DELAYED_TENSOR ? MODE_DELAYED : MODE_MX;
+      break;
+    default:
+      return fail(NORM_ERR_INVALID_ARG, "unknown scaling mode %d", scaling);
+  }
+  pl->rowwise = (qlayout & NORM_Q_ROWWISE) != 0;
+  pl->colwise = (qlayout & NORM_Q_COLWISE) != 0;
+
+  // layout choice
+  const int force_band = env_int("NORMFP8_FORCE_BAND", 0);
+  int row_cfg = -1;
+  const int row_override = env_int("NORMFP8_ROW_CFG", -1);
+  if (row_override >= 0 && row_override < ROW_NCFG && kRowShapes[row_override].cover() >= hidden) {
+    row_cfg = row_override;
+  } else {
+    const int pref[] = {ROW_W1_K1, ROW_W1_K2, ROW_W1_K4, ROW_W1_K8, ROW_W4_K4, ROW_W8_K4};
+    for (int c : pref)
+      if (kRowShapes[c].cover() >= hidden) {
+        row_cfg = c;
+        break;
+      }
+  }
+  pl->band = pl->colwise || row_cfg < 0 || force_band;
+  if (!pl->band) {
+    pl->cfg = row_cfg;
+  } else {
+    int bc;
+    if (pl->colwise) bc = hidden <= 512 ? BAND_R8_K1 : BAND_R8_K2;
+    else bc = hidden <= 2048 ? BAND_R1_K4 : BAND_R2_K8;
+    const int band_override = env_int("NORMFP8_BAND_CFG", -1);
+    if (band_override >= 0 && band_override < BAND_NCFG &&
+        (kBandShapes[band_override].colwise_ok || !pl->colwise) &&
+        !(pl->colwise && pl->mode == MODE_MX && kBandShapes[band_override].RW != 8))
+      bc = band_override;
+    pl->cfg = bc;
+    pl->S = (int)cdiv(hidden, kBandShapes[bc].cols());
+    pl->bands = cdiv(rows, kBandShapes[bc].rows());
+    if (pl->S > kMaxSlices)
+      return fail(NORM_ERR_UNSUPPORTED, "hidden %lld needs %d workgroups per band; this build allows %d",
+                  (long long)hidden, pl->S, kMaxSlices);
+  }
+
+  // workspace: header when the launch coordinates workgroups, then band partials
+  const bool header = pl->mode == MODE_DELAYED || (pl->band && pl->S > 1);
+  size_t ws = header ? (size_t)kWsHeaderBytes : 0;
+  if (pl->band && pl->S > 1) {
+    pl->partial_off = ws;
+    ws += round_up((size_t)pl->bands * pl->S * kBandShapes[pl->cfg].rows() * 2 * sizeof(float), 256);
+  }
+  pl->ws_bytes = ws;
+  (void)in_dtype;
+  (void)w_dtype;
+  return NORM_OK;
+}
+
+// ---------------------------------------------------------------- backward plan
+struct BwdPlan {
+  int cfg = 0;
+  int64_t G_max = 0;  // partial rows the workspace holds
+  size_t ws_bytes = 0;
+};
+
+constexpr int kMaxCus = 256;  // gfx950 (MI355X) compute units; bounds the workspace query
+
+int bwd_wgs_per_cu(int cfg) {
+  const int w = kBwdShapes[cfg].W;
+  return w >= 8 ? 1 : 8 / w;
+}
+
+int plan_bwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_type, int cu_margin,
+             BwdPlan *pl) {
+  if (rows < 0 || hidden <= 0) return fail(NORM_ERR_INVALID_ARG, "rows must be >= 0 and hidden > 0");
+  if (norm_type != NORM_LAYERNORM && norm_type != NORM_RMSNORM)
+    return fail(NORM_ERR_INVALID_ARG, "unknown norm_type %d", norm_type);
+  if (!is_hp(in_dtype)) return fail(NORM_ERR_UNSUPPORTED, "input dtype %d not supported", in_dtype);
+  if (!is_hp(w_dtype)) return fail(NORM_ERR_UNSUPPORTED, "weight dtype %d not supported", w_dtype);
+  if (cu_margin < 0) return fail(NORM_ERR_INVALID_ARG, "cu_margin must be >= 0");
+  if (hidden % 8 != 0) return fail(NORM_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 8", (long long)hidden);
+  int cfg = -1;
+  const int ov = env_int("NORMFP8_BWD_CFG", -1);
+  if (ov >= 0 && ov < BWD_NCFG && kBwdShapes[ov].cover() >= hidden) {
+    cfg = ov;
+  } else {
+    const int pref[] = {BWD_W2_K1, BWD_W4_K1, BWD_W4_K2, BWD_W8_K2, BWD_W16_K2};
+    for (int c : pref)
+      if (kBwdShapes[c].cover() >= hidden) {
+        cfg = c;
+        break;
+      }
+  }
+  if (cfg < 0)
+    return fail(NORM_ERR_UNSUPPORTED, "backward supports hidden <= %lld in this build",
+                (long long)kBwdShapes[BWD_W16_K2].cover());
+  pl->cfg = cfg;
+  const int64_t gmax = (int64_t)kMaxCus * bwd_wgs_per_cu(cfg);
+  pl->G_max = rows < gmax ? (rows > 0 ? rows : 1) : gmax;
+  const int arrays = norm_type == NORM_LAYERNORM ? 2 : 1;
+  pl->ws_bytes = kWsHeaderBytes + round_up((size_t)pl->G_max * hidden * arrays * sizeof(float), 256);
+  return NORM_OK;
+}
+
+int check_ws(void *ws, size_t have, size_t need) {
+  if (need == 0) return NORM_OK;
+  if (!ws) return fail(NORM_ERR_INVALID_ARG, "workspace is NULL but %zu bytes are required", need);
+  if (!aligned16(ws)) return fail(NORM_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  if (have < need) return fail(NORM_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", have, need);
+  return NORM_OK;
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+extern "C" {
+
+int norm_abi_version(void) { return NORMFP8_ABI_VERSION; }
+
+const char *norm_last_error(void) { return g_err.c_str(); }
+
+int norm_fwd_workspace_size(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype,
+                            int norm_type, int scaling, int qlayout, int zero_centered_gamma,
+                            float epsilon, int cu_margin, int is_training, size_t *bytes) {
+  (void)zero_centered_gamma;
+  (void)epsilon;
+  (void)is_training;
+  if (!bytes) return fail(NORM_ERR_INVALID_ARG, "bytes is NULL");
+  FwdPlan pl;
+  int rc = plan_fwd(rows, hidden, in_dtype, w_dtype, out_dtype, norm_type, scaling, qlayout, cu_margin, &pl);
+  if (rc) return rc;
+  *bytes = pl.ws_bytes;
+  return ok();
+}
+
+int norm_bwd_workspace_size(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_type,
+                            int zero_centered_gamma, float epsilon, int cu_margin, int with_add,
+                            size_t *bytes) {
+  (void)zero_centered_gamma;
+  (void)epsilon;
+  if (!bytes) return fail(NORM_ERR_INVALID_ARG, "bytes is NULL");
+  if (with_add && norm_type != NORM_RMSNORM)
+    return fail(NORM_ERR_INVALID_ARG, "the fused backward-add is defined for RMSNorm only");
+  BwdPlan pl;
+  int rc = plan_bwd(rows, hidden, in_dtype, w_dtype, norm_type, cu_margin, &pl);
+  if (rc) return rc;
+  *bytes = pl.ws_bytes;
+  return ok();
+}
+
+int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, const float *scale,
+             const float *amax, void *y, void *y_colwise, float *mu, float *rsigma, void *scale_inv,
+             void *colwise_scale_inv, float *updated_amax, void *workspace, size_t workspace_bytes,
+             int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
+             int scaling, int qlayout, int zero_centered_gamma, float epsilon, int cu_margin) {
+  FwdPlan pl;
+  int rc = plan_fwd(rows, hidden, in_dtype, w_dtype, out_dtype, norm_type, scaling, qlayout, cu_margin, &pl);
+  if (rc) return rc;
+  const bool ln = norm_type == NORM_LAYERNORM;
+  const bool any = rows > 0;  // with no rows, row-indexed buffers may be NULL
+  if ((any && !x) || !gamma) return fail(NORM_ERR_INVALID_ARG, "x and gamma are required");
+  if (ln && !beta) return fail(NORM_ERR_INVALID_ARG, "beta is required for LayerNorm");
+  if (!ln && beta) return fail(NORM_ERR_INVALID_ARG, "beta must be NULL for RMSNorm");
+  if (any && pl.rowwise && !y) return fail(NORM_ERR_INVALID_ARG, "rowwise output y is NULL");
+  if (!pl.rowwise && y) return fail(NORM_ERR_INVALID_ARG, "y must be NULL when rowwise output is not requested");
+  if (any && pl.colwise && !y_colwise) return fail(NORM_ERR_INVALID_ARG, "columnwise output y_colwise is NULL");
+  if (!pl.colwise && y_colwise) return fail(NORM_ERR_INVALID_ARG, "y_colwise must be NULL for a rowwise-only layout");
+  if (pl.mode == MODE_DELAYED) {
+    if (!scale || !amax || !updated_amax)
+      return fail(NORM_ERR_INVALID_ARG, "delayed scaling needs scale, amax and updated_amax");
+  }
+  if (pl.mode == MODE_DELAYED || (pl.mode == MODE_MX && any)) {
+    if (pl.rowwise && !scale_inv) return fail(NORM_ERR_INVALID_ARG, "scale_inv is required for rowwise output");
+    if (pl.colwise && !colwise_scale_inv)
+      return fail(NORM_ERR_INVALID_ARG, "colwise_scale_inv is required for columnwise output");
+  }
+  if (!(epsilon >= 0.0f)) return fail(NORM_ERR_INVALID_ARG, "epsilon must be >= 0");
+  for (const void *ptr : {x, gamma, beta, (const void *)y, (const void *)y_colwise})
+    if (ptr && !aligned16(ptr)) return fail(NORM_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+  rc = check_ws(workspace, workspace_bytes, pl.ws_bytes);
+  if (rc) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rows == 0) {
+    if (pl.mode != MODE_DELAYED) return ok();  // nothing to compute
+    // delayed scaling still publishes updated_amax = amax and scale_inv = 1/scale: one
+    // workgroup of the row kernel does that without visiting any row
+    pl.band = false;
+    pl.cfg = ROW_W1_K1;
+  }
+
+  DeviceInfo dev;
+  rc = device_info(&dev);
+  if (rc) return rc;
+  if (cu_margin >= dev.cus) return fail(NORM_ERR_INVALID_ARG, "cu_margin (%d) >= CU count (%d)", cu_margin, dev.cus);
+
+  FwdRowParams f{};
+  f.x = x;
+  f.gamma = gamma;
+  f.beta = beta;
+  f.scale = scale;
+  f.amax_in = amax;
+  f.y = y;
+  f.mu = ln ? mu : nullptr;
+  f.rsigma = rsigma;
+  f.scale_inv = scale_inv;
+  f.updated_amax = updated_amax;
+  f.ws = static_cast<uint32_t *>(workspace);
+  f.rows = rows;
+  f.hidden = hidden;
+  f.mx_cols = cdiv(hidden, 32);
+  f.w_dtype = w_dtype;
+  f.out_dtype = out_dtype;
+  f.zero_centered = zero_centered_gamma ? 1 : 0;
+  f.eps = epsilon;
+
+  if (!pl.band) {
+    const void *fn = fwd_row_kernel_ptr(norm_type, in_dtype, pl.mode, pl.cfg);
+    if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no forward row kernel for this combination");
+    const RowShape &sh = kRowShapes[pl.cfg];
+    int occ = 1;
+    rc = occupancy(fn, sh.threads(), &occ);
+    if (rc) return rc;
+    int64_t grid = cdiv(rows, sh.T);
+    const int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    rc = launch(fn, dim3((unsigned)grid), dim3(sh.threads()), &f, st);
+    if (rc) return rc;
+    return ok();
+  }
+
+  FwdBandParams b{};
+  b.f = f;
+  b.y_col = y_colwise;
+  b.col_scale_inv = colwise_scale_inv;
+  b.partials = pl.S > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.partial_off) : nullptr;
+  b.bands = pl.bands;
+  b.mx_rows = cdiv(rows, 32);
+  b.S = pl.S;
+  b.write_row = pl.rowwise ? 1 : 0;
+  const void *fn = fwd_band_kernel_ptr(norm_type, in_dtype, pl.mode, pl.colwise, pl.cfg);
+  if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no forward band kernel for this combination");
+  int64_t grid = pl.bands * pl.S;
+  if (grid < 1) grid = 1;  // rows == 0 with delayed scaling: one workgroup publishes amax / scale_inv
+  if (grid > 0x7fffffff) return fail(NORM_ERR_UNSUPPORTED, "too many tiles");
+  rc = launch(fn, dim3((unsigned)grid), dim3(256), &b, st);
+  if (rc) return rc;
+  return ok();
+}
+
+static int bwd_common(void *stream, bool with_add, const void *dy, const void *x, const void *residual, const float *mu,
+                      const float *rsigma, const void *gamma, void *dx, void *dgamma, void *dbeta,
+                      void *workspace, size_t workspace_bytes, int64_t rows, int64_t hidden, int in_dtype,
+                      int w_dtype, int norm_type, int zero_centered_gamma, int cu_margin) {
+  BwdPlan pl;
+  int rc = plan_bwd(rows, hidden, in_dtype, w_dtype, norm_type, cu_margin, &pl);
+  if (rc) return rc;
+  const bool ln = norm_type == NORM_LAYERNORM;
+  const bool any = rows > 0;  // with no rows, row-indexed buffers may be NULL
+  if ((any && (!dy || !x || !rsigma || !dx)) || !gamma || !dgamma)
+    return fail(NORM_ERR_INVALID_ARG, "dy, x, rsigma, gamma, dx and dgamma are required");
+  if (ln && ((any && !mu) || !dbeta)) return fail(NORM_ERR_INVALID_ARG, "LayerNorm backward needs mu and dbeta");
+  if (!ln && dbeta) return fail(NORM_ERR_INVALID_ARG, "dbeta must be NULL for RMSNorm");
+  for (const void *ptr : {dy, x, residual, gamma, (const void *)dx, (const void *)dgamma, (const void *)dbeta})
+    if (ptr && !aligned16(ptr)) return fail(NORM_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+  rc = check_ws(workspace, workspace_bytes, pl.ws_bytes);
+  if (rc) return rc;
+
+  DeviceInfo dev;
+  rc = device_info(&dev);
+  if (rc) return rc;
+  if (cu_margin >= dev.cus) return fail(NORM_ERR_INVALID_ARG, "cu_margin (%d) >= CU count (%d)", cu_margin, dev.cus);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  const void *fn = bwd_kernel_ptr(norm_type, in_dtype, with_add, pl.cfg);
+  if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no backward kernel for this combination");
+  const BwdShape &sh = kBwdShapes[pl.cfg];
+  int occ = 1;
+  rc = occupancy(fn, sh.threads(), &occ);
+  if (rc) return rc;
+  int64_t G = (int64_t)(dev.cus - cu_margin) * (occ < bwd_wgs_per_cu(pl.cfg) ? occ : bwd_wgs_per_cu(pl.cfg));
+  if (G > pl.G_max) G = pl.G_max;
+  if (G > rows) G = rows;
+  if (G < 1) G = 1;
+
+  BwdParams p{};
+  p.dy = dy;
+  p.x = x;
+  p.residual = residual;
+  p.mu = ln ? mu : nullptr;
+  p.rsigma = rsigma;
+  p.gamma = gamma;
+  p.dx = dx;
+  p.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + kWsHeaderBytes);
+  p.rows = rows;
+  p.hidden = hidden;
+  p.w_dtype = w_dtype;
+  p.zero_centered = zero_centered_gamma ? 1 : 0;
+  p.G = (int)G;
+  // rows == 0: the row kernel has no rows to visit but still writes zero partials, so the
+  // finalize step returns zero gradients
+  rc = launch(fn, dim3((unsigned)G), dim3(sh.threads()), &p, st);
+  if (rc) return rc;
+
+  FinalizeParams fp{};
+  fp.part = p.part;
+  fp.dgamma = dgamma;
+  fp.dbeta = ln ? dbeta : nullptr;
+  fp.hidden = hidden;
+  fp.G = (int)G;
+  fp.w_dtype = w_dtype;
+  rc = launch(bwd_finalize_kernel_ptr(), dim3((unsigned)cdiv(hidden, 32), ln ? 2 : 1), dim3(256), &fp, st);
+  if (rc) return rc;
+  return ok();
+}
+
+int norm_bwd(void *stream, const void *dy, const void *x, const float *mu, const float *rsigma,
+             const void *gamma, void *dx, void *dgamma, void *dbeta, void *workspace,
+             size_t workspace_bytes, int64_t rows, int64_t hidden, int in_dtype, int w_dtype,
+             int norm_type, int zero_centered_gamma, int cu_margin) {
+  return bwd_common(stream, false, dy, x, nullptr, mu, rsigma, gamma, dx, dgamma, dbeta, workspace, workspace_bytes,
+                    rows, hidden, in_dtype, w_dtype, norm_type, zero_centered_gamma, cu_margin);
+}
+
+int norm_bwd_add(void *stream, const void *dy, const void *x, const void *residual_dy, const float *rsigma,
+                 const void *gamma, void *dx, void *dgamma, void *workspace, size_t workspace_bytes,
+                 int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int zero_centered_gamma,
+                 int cu_margin) {
+  if (!residual_dy && rows > 0) return fail(NORM_ERR_INVALID_ARG, "residual_dy is required");
+  return bwd_common(stream, true, dy, x, residual_dy, nullptr, rsigma, gamma, dx, dgamma, nullptr, workspace,
+                    workspace_bytes, rows, hidden, in_dtype, w_dtype, NORM_RMSNORM, zero_centered_gamma,
+                    cu_margin);
+}
+
+int norm_workspace_init(void *stream, void *workspace, size_t workspace_bytes) {
+  if (!workspace) return fail(NORM_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(NORM_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  if (workspace_bytes < (size_t)kWsHeaderBytes)
+    return fail(NORM_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than the %d-byte header", kWsHeaderBytes);
+  uint32_t *ws = static_cast<uint32_t *>(workspace);
+  void *args[] = {&ws};
+  hipError_t e = hipLaunchKernel(ws_init_kernel_ptr(), dim3(1), dim3(256), args, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(NORM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int norm_workspace_check(void *stream, void *workspace, uint32_t *flags) {
+  if (!workspace || !flags) return fail(NORM_ERR_INVALID_ARG, "workspace and flags are required");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(NORM_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  uint32_t words[4] = {0, 0, 0, 0};
+  e = hipMemcpy(words, workspace, sizeof(words), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(NORM_ERR_HIP, "hipMemcpy: %s", hipGetErrorString(e));
+  uint32_t f = words[kWsError];
+  if (words[kWsDone] != 0 || words[kWsTicket] != 0 || words[kWsAmax] != 0) f |= 2u;
+  *flags = f;
+  if (f) {
+    e = hipMemset(static_cast<char *>(workspace) + kWsError * 4, 0, 4);
+    if (e != hipSuccess) return fail(NORM_ERR_HIP, "hipMemset: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,241 @@
+// bwd.hip -- LayerNorm / RMSNorm backward (optionally fused with the residual-gradient add)
+// and the weight-gradient finalize kernel.
+//
+// [XLA-Norm] = "Implementation: NVIDIA TransformerEngine JAX XLA Normalization";
+// [BwdAdd]   = "Implementation: NVIDIA TransformerEngine Ops Fused Backward Add RMSNorm";
+// [NVRTC-PR] = "Migrate norms and softmax kernels to NVRTC" (TransformerEngine pull request).
+// [XLA-Norm] Description: the backward dispatch for both norm types. [NVRTC-PR] file table
+// and Flowchart: the backward kernels leave per-CTA weight-gradient partials ("semi" kernels)
+// and a finalize kernel reduces them. [BwdAdd] Overview / Description / I/O Contract: the
+// RMSNorm backward adds the residual branch's gradient into dx inside the same kernel, and
+// returns the weight gradient.
+//
+// Work split: all W waves of a workgroup work on one row at a time; lane t owns the strips
+// t + 64 * W * k. The grid is persistent (G workgroups, rows g, g + G, ...), so each lane keeps
+// its columns' gamma and its dgamma / dbeta partial sums in registers across rows and writes
+// them once; the finalize kernel adds the G partial rows in a fixed order (deterministic).
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace nf8 {
+
+template <int NORM, class IN, bool ADD, int W, int KC>
+__global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
+  constexpr int NT = 64 * W;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t H = p.hidden;
+
+  bool cv[KC];
+  float g[KC][8], dg[KC][8], db[NORM == NT_LAYERNORM ? KC : 1][8];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    const int64_t col = 8 * (int64_t)(tid + NT * k);
+    cv[k] = col < H;
+    if (cv[k]) {
+      load_w8(g[k], p.gamma, col, p.w_dtype);
+      if (p.zero_centered) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[k][i] += 1.0f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g[k][i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      dg[k][i] = 0.0f;
+      if constexpr (NORM == NT_LAYERNORM) db[k][i] = 0.0f;
+    }
+  }
+
+  __shared__ float red[2][W][2];
+  const float inv_h = 1.0f / (float)H;
+
+  int iter = 0;
+  for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x, ++iter) {
+    Strip<IN> dys[KC], xs[KC], rsd[ADD ? KC : 1];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int64_t off = row * H + 8 * (int64_t)(tid + NT * k);
+      if (cv[k]) {
+        load_strip<IN>(dys[k], p.dy, off);
+        load_strip<IN>(xs[k], p.x, off);
+        if constexpr (ADD) load_strip<IN>(rsd[k], p.residual, off);
+      } else {
+        zero_strip<IN>(dys[k]);
+        zero_strip<IN>(xs[k]);
+        if constexpr (ADD) zero_strip<IN>(rsd[k]);
+      }
+    }
+    const float rs = p.rsigma[row];
+    const float mu = NORM == NT_LAYERNORM ? p.mu[row] : 0.0f;
+
+    // row sums of w = dy * g and w * xhat
+    float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      float dv[8], xv[8];
+      strip_to_f32<IN>(dys[k], dv);
+      strip_to_f32<IN>(xs[k], xv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xh = (xv[i] - mu) * rs;
+        const float w = dv[i] * g[k][i];
+        s1 += w;
+        s2 = fmaf(w, xh, s2);
+      }
+    }
+    if constexpr (NORM == NT_LAYERNORM) s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    if constexpr (W > 1) {
+      if (lane == 0) {
+        red[iter & 1][wave][0] = s1;
+        red[iter & 1][wave][1] = s2;
+      }
+      __syncthreads();
+      s1 = red[iter & 1][0][0];
+      s2 = red[iter & 1][0][1];
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        s1 += red[iter & 1][w][0];
+        s2 += red[iter & 1][w][1];
+      }
+    }
+    const float c1 = NORM == NT_LAYERNORM ? s1 * inv_h : 0.0f;
+    const float c2 = s2 * inv_h;
+
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      float dv[8], xv[8], out[8];
+      strip_to_f32<IN>(dys[k], dv);
+      strip_to_f32<IN>(xs[k], xv);
+      float rv[8];
+      if constexpr (ADD) strip_to_f32<IN>(rsd[k], rv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xh = (xv[i] - mu) * rs;
+        const float w = dv[i] * g[k][i];
+        float d = rs * (w - fmaf(xh, c2, c1));
+        if constexpr (ADD) d += rv[i];
+        out[i] = d;
+        dg[k][i] = fmaf(dv[i], xh, dg[k][i]);
+        if constexpr (NORM == NT_LAYERNORM) db[k][i] += dv[i];
+      }
+      if (cv[k]) store_t8<IN>(p.dx, row * H + 8 * (int64_t)(tid + NT * k), out);
+    }
+  }
+
+  // this workgroup's partial weight gradients
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    if (!cv[k]) continue;
+    const int64_t col = 8 * (int64_t)(tid + NT * k);
+    float4 *dst = reinterpret_cast<float4 *>(p.part + (int64_t)blockIdx.x * H + col);
+    dst[0] = make_float4(dg[k][0], dg[k][1], dg[k][2], dg[k][3]);
+    dst[1] = make_float4(dg[k][4], dg[k][5], dg[k][6], dg[k][7]);
+    if constexpr (NORM == NT_LAYERNORM) {
+      float4 *dsb = reinterpret_cast<float4 *>(p.part + ((int64_t)p.G + blockIdx.x) * H + col);
+      dsb[0] = make_float4(db[k][0], db[k][1], db[k][2], db[k][3]);
+      dsb[1] = make_float4(db[k][4], db[k][5], db[k][6], db[k][7]);
+    }
+  }
+}
+
+// Fixed-order reduction of the G partial rows. Workgroup (x, y) owns 32 columns of array y
+// (0: dgamma, 1: dbeta); thread (c, q) adds 4 columns (one float4) of partial rows q, q + 32,
+// q + 64, ... with four loads in flight, and the 32 sums per column are added in q order. The
+// grid has H / 32 workgroups per array so the whole chip streams the partials.
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(FinalizeParams p) {
+  constexpr int Q = 32;
+  const int c = threadIdx.x & 7;
+  const int q = threadIdx.x >> 3;
+  const int64_t col = (int64_t)blockIdx.x * 32 + 4 * c;
+  const int which = blockIdx.y;
+  const float *part = p.part + (int64_t)which * p.G * p.hidden;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (col < p.hidden) {
+    int g = q;
+    for (; g + 3 * Q < p.G; g += 4 * Q) {
+      const float4 a = *reinterpret_cast<const float4 *>(part + (int64_t)g * p.hidden + col);
+      const float4 b = *reinterpret_cast<const float4 *>(part + (int64_t)(g + Q) * p.hidden + col);
+      const float4 e = *reinterpret_cast<const float4 *>(part + (int64_t)(g + 2 * Q) * p.hidden + col);
+      const float4 f = *reinterpret_cast<const float4 *>(part + (int64_t)(g + 3 * Q) * p.hidden + col);
+      s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+      s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
+      s.x += e.x; s.y += e.y; s.z += e.z; s.w += e.w;
+      s.x += f.x; s.y += f.y; s.z += f.z; s.w += f.w;
+    }
+    for (; g < p.G; g += Q) {
+      const float4 a = *reinterpret_cast<const float4 *>(part + (int64_t)g * p.hidden + col);
+      s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+    }
+  }
+  __shared__ float4 red[Q][8];
+  red[q][c] = s;
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    const int cc = threadIdx.x >> 2, e = threadIdx.x & 3;
+    const int64_t out = (int64_t)blockIdx.x * 32 + threadIdx.x;
+    if (out < p.hidden) {
+      float t = 0.0f;
+      for (int w = 0; w < Q; ++w) {
+        const float4 v = red[w][cc];
+        t += e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+      }
+      void *dst = which == 0 ? p.dgamma : p.dbeta;
+      if (p.w_dtype == DT_F32) {
+        static_cast<float *>(dst)[out] = t;
+      } else if (p.w_dtype == DT_BF16) {
+        __bf16 h = (__bf16)t;
+        static_cast<uint16_t *>(dst)[out] = __builtin_bit_cast(uint16_t, h);
+      } else {
+        _Float16 h = (_Float16)t;
+        static_cast<uint16_t *>(dst)[out] = __builtin_bit_cast(uint16_t, h);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+
+template <int NORM, class IN, bool ADD>
+static const void *pick_bwd_cfg(int cfg) {
+  switch (cfg) {
+    case BWD_W2_K1: return (const void *)bwd_kernel<NORM, IN, ADD, 2, 1>;
+    case BWD_W4_K1: return (const void *)bwd_kernel<NORM, IN, ADD, 4, 1>;
+    case BWD_W4_K2: return (const void *)bwd_kernel<NORM, IN, ADD, 4, 2>;
+    case BWD_W8_K2: return (const void *)bwd_kernel<NORM, IN, ADD, 8, 2>;
+    case BWD_W16_K2: return (const void *)bwd_kernel<NORM, IN, ADD, 16, 2>;
+    case BWD_W8_K1: return (const void *)bwd_kernel<NORM, IN, ADD, 8, 1>;
+    case BWD_W16_K1: return (const void *)bwd_kernel<NORM, IN, ADD, 16, 1>;
+    case BWD_W4_K4: return (const void *)bwd_kernel<NORM, IN, ADD, 4, 4>;
+    default: return nullptr;
+  }
+}
+
+template <int NORM, bool ADD>
+static const void *pick_bwd_in(int in_dtype, int cfg) {
+  switch (in_dtype) {
+    case DT_F32: return pick_bwd_cfg<NORM, F32, ADD>(cfg);
+    case DT_BF16: return pick_bwd_cfg<NORM, BF16, ADD>(cfg);
+    case DT_F16: return pick_bwd_cfg<NORM, F16, ADD>(cfg);
+    default: return nullptr;
+  }
+}
+
+const void *bwd_kernel_ptr(int norm, int in_dtype, bool add, int cfg) {
+  if (norm == NT_LAYERNORM) return add ? nullptr : pick_bwd_in<NT_LAYERNORM, false>(in_dtype, cfg);
+  return add ? pick_bwd_in<NT_RMSNORM, true>(in_dtype, cfg) : pick_bwd_in<NT_RMSNORM, false>(in_dtype, cfg);
+}
+
+const void *bwd_finalize_kernel_ptr() { return (const void *)bwd_finalize_kernel; }
+
+// zero the workspace header
+__global__ __launch_bounds__(256) void ws_init_kernel(uint32_t *ws) {
+  for (int i = threadIdx.x; i < kWsHeaderBytes / 4; i += 256) ws[i] = 0u;
+}
+const void *ws_init_kernel_ptr() { return (const void *)ws_init_kernel; }
+
+}  // namespace nf8

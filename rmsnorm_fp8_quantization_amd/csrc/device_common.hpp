@@ -1,0 +1,324 @@
+// device_common.hpp -- element conversions, strip loads/stores, cross-lane reductions and
+// cross-workgroup synchronisation shared by the gfx950 normalisation kernels.
+//
+// Pages cited (by title and section):
+//   [XLA-Norm]  "Implementation: NVIDIA TransformerEngine JAX XLA Normalization"
+//   [BwdAdd]    "Implementation: NVIDIA TransformerEngine Ops Fused Backward Add RMSNorm"
+//   [NVRTC-PR]  "Migrate norms and softmax kernels to NVRTC" (TransformerEngine pull request)
+//
+// Data layout used by every kernel: a "strip" is 8 consecutive elements of one row, i.e. one
+// 16-byte vector for 16-bit inputs (two for float32). A lane owns whole strips; consecutive
+// lanes own consecutive strips so a wave's loads and stores are contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+
+namespace nf8 {
+
+// ------------------------------------------------------------------------------------------
+// element types
+// ------------------------------------------------------------------------------------------
+
+struct F32 {
+  static constexpr int code = DT_F32;
+  static constexpr int bytes = 4;
+};
+struct F16 {
+  static constexpr int code = DT_F16;
+  static constexpr int bytes = 2;
+};
+struct BF16 {
+  static constexpr int code = DT_BF16;
+  static constexpr int bytes = 2;
+};
+
+// Raw storage of one strip: 16 bytes for 16-bit types, 32 bytes for float32.
+template <class T> struct Strip;
+template <> struct Strip<F32> { uint4 v[2]; };
+template <> struct Strip<F16> { uint4 v[1]; };
+template <> struct Strip<BF16> { uint4 v[1]; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+template <class T> __device__ __forceinline__ void strip_to_f32(const Strip<T> &s, float (&o)[8]);
+template <> __device__ __forceinline__ void strip_to_f32<F32>(const Strip<F32> &s, float (&o)[8]) {
+  o[0] = __uint_as_float(s.v[0].x); o[1] = __uint_as_float(s.v[0].y);
+  o[2] = __uint_as_float(s.v[0].z); o[3] = __uint_as_float(s.v[0].w);
+  o[4] = __uint_as_float(s.v[1].x); o[5] = __uint_as_float(s.v[1].y);
+  o[6] = __uint_as_float(s.v[1].z); o[7] = __uint_as_float(s.v[1].w);
+}
+template <> __device__ __forceinline__ void strip_to_f32<BF16>(const Strip<BF16> &s, float (&o)[8]) {
+  o[0] = bf16_lo(s.v[0].x); o[1] = bf16_hi(s.v[0].x);
+  o[2] = bf16_lo(s.v[0].y); o[3] = bf16_hi(s.v[0].y);
+  o[4] = bf16_lo(s.v[0].z); o[5] = bf16_hi(s.v[0].z);
+  o[6] = bf16_lo(s.v[0].w); o[7] = bf16_hi(s.v[0].w);
+}
+template <> __device__ __forceinline__ void strip_to_f32<F16>(const Strip<F16> &s, float (&o)[8]) {
+  o[0] = f16_lo(s.v[0].x); o[1] = f16_hi(s.v[0].x);
+  o[2] = f16_lo(s.v[0].y); o[3] = f16_hi(s.v[0].y);
+  o[4] = f16_lo(s.v[0].z); o[5] = f16_hi(s.v[0].z);
+  o[6] = f16_lo(s.v[0].w); o[7] = f16_hi(s.v[0].w);
+}
+
+template <class T>
+__device__ __forceinline__ void load_strip(Strip<T> &s, const void *base, int64_t elem) {
+  const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + elem * T::bytes);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(Strip<T>) / 16); ++i) s.v[i] = p[i];
+}
+template <class T> __device__ __forceinline__ void zero_strip(Strip<T> &s) {
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(Strip<T>) / 16); ++i) s.v[i] = make_uint4(0, 0, 0, 0);
+}
+
+// 8 weights (gamma or beta) of runtime dtype -> float32
+__device__ __forceinline__ void load_w8(float (&o)[8], const void *base, int64_t elem, int dt) {
+  if (dt == DT_F32) {
+    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem);
+    float4 a = p[0], b = p[1];
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  } else {
+    Strip<BF16> s;
+    load_strip<BF16>(s, base, elem);
+    if (dt == DT_BF16) {
+      strip_to_f32<BF16>(s, o);
+    } else {
+      Strip<F16> h;
+      h.v[0] = s.v[0];
+      strip_to_f32<F16>(h, o);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 ha = (__bf16)a, hb = (__bf16)b;  // v_cvt_pk_bf16_f32: nearest-even
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// store 8 float32 values as runtime out dtype (F32 / F16 / BF16) at element offset `elem`
+__device__ __forceinline__ void store_out8(void *base, int64_t elem, const float (&y)[8], int dt) {
+  if (dt == DT_F32) {
+    float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(base) + elem);
+    p[0] = make_float4(y[0], y[1], y[2], y[3]);
+    p[1] = make_float4(y[4], y[5], y[6], y[7]);
+  } else if (dt == DT_BF16) {
+    uint4 *p = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + elem);
+    *p = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                    pack_bf16x2(y[6], y[7]));
+  } else {
+    uint4 *p = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + elem);
+    *p = make_uint4(pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]), pack_f16x2(y[4], y[5]),
+                    pack_f16x2(y[6], y[7]));
+  }
+}
+
+// store 8 float32 values in the storage type T (used for dx)
+template <class T> __device__ __forceinline__ void store_t8(void *base, int64_t elem, const float (&y)[8]) {
+  store_out8(base, elem, y, T::code);
+}
+
+// ------------------------------------------------------------------------------------------
+// FP8 (OCP E4M3 / E5M2). gfx950's v_cvt_pk_{fp8,bf8}_f32 convert to the OCP encodings with
+// round-to-nearest-even; inputs are clamped to the largest finite value first so that
+// out-of-range values saturate (the oracle's reading) rather than depend on the converter's
+// overflow behaviour.
+// ------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float fp8_max(int fmt) { return fmt == DT_E4M3 ? 448.0f : 57344.0f; }
+
+// 8 float32 -> 8 FP8 codes packed little-endian in two dwords
+__device__ __forceinline__ uint2 fp8_pack8(const float (&u)[8], int fmt) {
+  const float m = fp8_max(fmt);
+  float c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(u[i], -m, m);
+  int w0, w1;
+  if (fmt == DT_E4M3) {
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w0, true);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], w1, true);
+  } else {
+    w0 = __builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], w0, true);
+    w1 = __builtin_amdgcn_cvt_pk_bf8_f32(c[4], c[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_bf8_f32(c[6], c[7], w1, true);
+  }
+  return make_uint2((uint32_t)w0, (uint32_t)w1);
+}
+
+// MXFP8 shared exponent X of a block whose largest magnitude is `a` (float32, a >= 0):
+// X = clamp(floor(log2 a) - emax, -127, 127); a zero or subnormal maximum gives -127.
+// floor(log2 a) of a normal float32 is its unbiased exponent field.
+__device__ __forceinline__ int mx_exponent(float a, int fmt) {
+  const int emax = fmt == DT_E4M3 ? 8 : 15;
+  int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127 - emax;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// 2^-X as float32 (X in [-127, 127] keeps the biased exponent 127 - X in [0, 254]; X = 127 gives
+// 2^-127, a subnormal, built from the bit pattern)
+__device__ __forceinline__ float exp2_neg(int x) {
+  int b = 127 - x;
+  return b > 0 ? __uint_as_float((uint32_t)b << 23) : __uint_as_float(0x00400000u);
+}
+
+// ------------------------------------------------------------------------------------------
+// cross-lane reductions (wave64). Quad and row steps use DPP; the 16- and 32-lane steps use
+// ds_swizzle / ds_bpermute. Every lane ends with the same value: each step combines a lane
+// with a partner using a commutative operation.
+// ------------------------------------------------------------------------------------------
+
+#define NF8_DPP(ctrl) \
+  __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), ctrl, 0xf, 0xf, false))
+
+__device__ __forceinline__ float xor1(float v) { return NF8_DPP(0xB1); }   // quad_perm [1,0,3,2]
+__device__ __forceinline__ float xor2(float v) { return NF8_DPP(0x4E); }   // quad_perm [2,3,0,1]
+__device__ __forceinline__ float hmirror(float v) { return NF8_DPP(0x141); } // row_half_mirror
+__device__ __forceinline__ float mirror(float v) { return NF8_DPP(0x140); }  // row_mirror
+__device__ __forceinline__ float xor16(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_ds_swizzle((int)__float_as_uint(v), (16 << 10) | 0x1f));
+}
+__device__ __forceinline__ float xor32(float v) {
+  int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, (int)__float_as_uint(v)));
+}
+#undef NF8_DPP
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += xor1(v);
+  v += xor2(v);
+  v += hmirror(v);
+  v += mirror(v);
+  v += xor16(v);
+  v += xor32(v);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, xor1(v));
+  v = fmaxf(v, xor2(v));
+  v = fmaxf(v, hmirror(v));
+  v = fmaxf(v, mirror(v));
+  v = fmaxf(v, xor16(v));
+  v = fmaxf(v, xor32(v));
+  return v;
+}
+// max over aligned groups of 4 lanes (one 32-element MX block = 4 strips)
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, xor1(v));
+  v = fmaxf(v, xor2(v));
+  return v;
+}
+
+// Partial statistics of a set of elements: count, mean and sum of squared deviations (the
+// parallel-variance form that merges in one step). RMSNorm uses only `m2` as the sum of
+// squares (n and mean unused).
+struct Stats {
+  float n, mean, m2;
+};
+
+// Chan et al. pairwise merge. Callers always pass the partner from the lower lane / wave /
+// workgroup as `a`, so both partners compute bit-identical results.
+__device__ __forceinline__ Stats chan_merge(const Stats &a, const Stats &b) {
+  const float n = a.n + b.n;
+  if (b.n == 0.0f) return a;
+  if (a.n == 0.0f) return b;
+  const float d = b.mean - a.mean;
+  const float fb = b.n / n;
+  Stats r;
+  r.n = n;
+  r.mean = fmaf(d, fb, a.mean);
+  r.m2 = a.m2 + b.m2 + d * d * (a.n * fb);
+  return r;
+}
+
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// wave-wide Chan merge; partner order fixed by lane position
+__device__ __forceinline__ Stats wave_merge(Stats s) {
+  const int lane = lane_id();
+#define NF8_STEP(FN, LOW)                                   \
+  {                                                         \
+    Stats o{FN(s.n), FN(s.mean), FN(s.m2)};                 \
+    s = (LOW) ? chan_merge(s, o) : chan_merge(o, s);        \
+  }
+  NF8_STEP(xor1, (lane & 1) == 0)
+  NF8_STEP(xor2, (lane & 2) == 0)
+  NF8_STEP(hmirror, (lane & 7) < 4)
+  NF8_STEP(mirror, (lane & 15) < 8)
+  NF8_STEP(xor16, (lane & 16) == 0)
+  NF8_STEP(xor32, (lane & 32) == 0)
+#undef NF8_STEP
+  return s;
+}
+
+// ------------------------------------------------------------------------------------------
+// cross-workgroup synchronisation through the workspace header
+//
+// gfx950 keeps one L2 per XCD and agent-scope fences write back / invalidate the whole L2, so
+// the exchange avoids them: every word that crosses workgroups is written and read with
+// agent-scope atomic operations (cache-coherent at device scope), and ordering between a
+// workgroup's data writes and its counter update is enforced with a wait for outstanding
+// memory operations plus a workgroup-scope fence.
+// ------------------------------------------------------------------------------------------
+
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t max_dev(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t xchg_dev(uint32_t *p, uint32_t v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void or_dev(uint32_t *p, uint32_t v) {
+  __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// wait until this wave's outstanding vector-memory operations have completed, then order
+// later memory operations after them (workgroup scope: no cache maintenance)
+__device__ __forceinline__ void vmem_drain() {
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));  // vmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+}
+
+// Spin until *p >= target. Gives up after `limit` ticks of the 100 MHz real-time counter and
+// records the time-out in the header's error word (the caller then proceeds with whatever
+// partner data is present, so a corrupt header cannot hang the GPU).
+__device__ __forceinline__ void spin_until_ge(const uint32_t *p, uint32_t target, uint32_t *err) {
+  if (ld_dev_u32(p) >= target) return;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (ld_dev_u32(p) < target) {
+    __builtin_amdgcn_s_sleep(2);
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
+      or_dev(err, 1u);
+      return;
+    }
+  }
+}
+
+}  // namespace nf8

@@ -1,0 +1,453 @@
+// fwd_band.hip -- LayerNorm / RMSNorm forward over tiles of several rows, for columnwise
+// (transposed) FP8 outputs and for rows too long for one workgroup.
+//
+// [XLA-Norm] = "Implementation: NVIDIA TransformerEngine JAX XLA Normalization";
+// [NVRTC-PR] = "Migrate norms and softmax kernels to NVRTC" (TransformerEngine pull request).
+// [XLA-Norm] Description: rowwise and optional columnwise FP8 outputs, each with its own
+// scale_inv, for delayed tensor scaling and MXFP8 block scaling. [NVRTC-PR] Flowchart and
+// review discussion: rows too long for one CTA are split over several CTAs that combine their
+// statistics through a workspace and a barrier.
+//
+// Work split: a workgroup (4 waves) owns a tile of R = 4 * RW rows x CW = 512 * KC columns;
+// wave w owns rows [w*RW, (w+1)*RW) of the tile and lane l the strips l + 64k. S workgroups
+// cover one band of R full rows. Each keeps its tile in registers (x is read from HBM once),
+// computes per-row partial statistics, publishes them in the workspace and waits for the other
+// S - 1 workgroups of its band; every workgroup then merges the S partials in slice order, so
+// all S hold bit-identical statistics.
+//
+// Tiles are handed out in ticket order (an atomic counter taken when the workgroup starts), so
+// the workgroups of a band are always co-resident: at any time only the newest band can be
+// waiting for a member that has not started yet, and every older band's members are running.
+//
+// Columnwise outputs: y_col is [hidden, rows]. MXFP8 columnwise blocks are the 32 rows of one
+// band (RW = 8): each lane takes the max over its 8 rows per column, the 4 waves combine
+// through LDS, and every lane writes its 8 rows of each column as one 8-byte store after an
+// in-register byte transpose.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace nf8 {
+
+// 4x4 byte transpose of (a0..a3): result i holds byte i of a0, a1, a2, a3
+__device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                             uint32_t (&o)[4]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// codes[j] = 8 codes of row j (columns 0..7); write column i's RW codes to colp + i * ld
+template <int RW>
+__device__ __forceinline__ void store_col_codes(const uint2 (&codes)[RW], uint8_t *colp, int64_t ld,
+                                                int valid_rows, bool aligned) {
+  static_assert(RW == 4 || RW == 8, "columnwise tiles hold 4 or 8 rows per wave");
+  uint32_t lo[RW == 8 ? 2 : 1][4], hi[RW == 8 ? 2 : 1][4];
+#pragma unroll
+  for (int h = 0; h < RW / 4; ++h) {
+    transpose4x4(codes[4 * h].x, codes[4 * h + 1].x, codes[4 * h + 2].x, codes[4 * h + 3].x, lo[h]);
+    transpose4x4(codes[4 * h].y, codes[4 * h + 1].y, codes[4 * h + 2].y, codes[4 * h + 3].y, hi[h]);
+  }
+  if (aligned && valid_rows == RW) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint8_t *dst = colp + i * ld;
+      const uint32_t w0 = i < 4 ? lo[0][i] : hi[0][i - 4];
+      if constexpr (RW == 8) {
+        const uint32_t w1 = i < 4 ? lo[1][i] : hi[1][i - 4];
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(w0, w1);
+      } else {
+        *reinterpret_cast<uint32_t *>(dst) = w0;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint8_t *dst = colp + i * ld;
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const uint32_t w = i < 4 ? lo[j / 4][i] : hi[j / 4][i - 4];
+        if (j < valid_rows) dst[j] = (uint8_t)(w >> (8 * (j & 3)));
+      }
+    }
+  }
+}
+
+template <int NORM, class IN, int MODE, int RW, int KC, bool COL>
+__global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
+  constexpr int R = 4 * RW;
+  constexpr int CW = 512 * KC;
+  constexpr bool MXCOL = COL && MODE == MODE_MX;
+  const FwdRowParams &p = bp.f;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int S = bp.S;
+  const int64_t H = p.hidden;
+  const int64_t N = p.rows;
+  const int fmt = p.out_dtype;
+
+  __shared__ int64_t s_ticket;
+  __shared__ uint32_t s_last;
+  __shared__ float colmax[MXCOL ? 4 : 1][MXCOL ? CW : 1];
+  __shared__ float xpart[4][RW][kMaxSlices][2];  // fetched partials of the band's rows
+
+  int64_t band;
+  int slice;
+  if (S == 1) {
+    band = blockIdx.x;
+    slice = 0;
+  } else {
+    if (tid == 0) s_ticket = (int64_t)add_dev(p.ws + kWsTicket, 1u);
+    __syncthreads();
+    const int64_t t = s_ticket;
+    band = t / S;
+    slice = (int)(t - band * S);
+  }
+  const int64_t rbase = band * R + wave * RW;  // first row of this wave
+  const int64_t cbase = (int64_t)slice * CW;
+
+  // Weights are read per strip where they are used (they stay in L1/L2 for the tile's rows)
+  // instead of being held in registers for every strip of the tile.
+  bool cv[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) cv[k] = cbase + 8 * (lane + 64 * k) < H;
+  auto weights = [&](int k, float (&g)[8], float (&bt)[8]) {
+    const int64_t col = cbase + 8 * (lane + 64 * k);
+    if (cv[k]) {
+      load_w8(g, p.gamma, col, p.w_dtype);
+      if (p.zero_centered) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[i] += 1.0f;
+      }
+      if constexpr (NORM == NT_LAYERNORM) load_w8(bt, p.beta, col, p.w_dtype);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        g[i] = 0.0f;
+        bt[i] = 0.0f;
+      }
+    }
+  };
+
+  Strip<IN> xs[RW][KC];
+#pragma unroll
+  for (int j = 0; j < RW; ++j)
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int64_t row = rbase + j;
+      if (row < N && cv[k]) load_strip<IN>(xs[j][k], p.x, row * H + cbase + 8 * (lane + 64 * k));
+      else zero_strip<IN>(xs[j][k]);
+    }
+
+  // ---- per-row partial statistics of this slice (wave-merged)
+  Stats st[RW];
+#pragma unroll
+  for (int j = 0; j < RW; ++j) {
+    const bool rv = rbase + j < N;
+    if constexpr (NORM == NT_LAYERNORM) {
+      float s = 0.0f, n = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float xv[8];
+        strip_to_f32<IN>(xs[j][k], xv);
+        if (rv && cv[k]) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s += xv[i];
+          n += 8.0f;
+        }
+      }
+      const float m = n > 0.0f ? s / n : 0.0f;
+      float q = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float xv[8];
+        strip_to_f32<IN>(xs[j][k], xv);
+        if (rv && cv[k]) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float d = xv[i] - m;
+            q = fmaf(d, d, q);
+          }
+        }
+      }
+      st[j] = wave_merge(Stats{n, m, q});
+    } else {
+      float q = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float xv[8];
+        strip_to_f32<IN>(xs[j][k], xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q = fmaf(xv[i], xv[i], q);
+      }
+      st[j] = Stats{0.0f, 0.0f, wave_sum(q)};
+    }
+  }
+
+  // ---- combine the S slices of the band through the workspace
+  if (S > 1) {
+    float *part = bp.partials + (band * S + slice) * (int64_t)R * 2;
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      if (lane == j) {
+        st_dev(part + 2 * (wave * RW + j), st[j].mean);
+        st_dev(part + 2 * (wave * RW + j) + 1, st[j].m2);
+      }
+    }
+    vmem_drain();
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t *slot = p.ws + kWsSlot0 + (band % kWsSlots);
+      const uint32_t q = (uint32_t)(band / kWsSlots);
+      uint32_t *err = p.ws + kWsError;
+      spin_until_ge(slot, q * (uint32_t)S, err);  // previous band on this slot has arrived
+      add_dev(slot, 1u);
+      spin_until_ge(slot, (q + 1) * (uint32_t)S, err);  // all S slices of this band arrived
+    }
+    __syncthreads();
+    // every lane fetches one (row, slice) partial at once; lane j then merges row j's S
+    // partials in slice order from LDS and broadcasts the result to the wave
+    const float *bpart = bp.partials + band * S * (int64_t)R * 2;
+    for (int l = lane; l < RW * S; l += 64) {
+      const int j = l / S, s = l - (l / S) * S;
+      const float *e = bpart + ((int64_t)s * R + wave * RW + j) * 2;
+      xpart[wave][j][s][0] = ld_dev(e);
+      xpart[wave][j][s][1] = ld_dev(e + 1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      Stats acc{0.0f, 0.0f, 0.0f};
+      if (lane == j) {
+        for (int s = 0; s < S; ++s) {
+          const float mean = xpart[wave][j][s][0], m2 = xpart[wave][j][s][1];
+          if constexpr (NORM == NT_LAYERNORM) {
+            const int64_t left = H - (int64_t)s * CW;
+            const float n = (float)(left < CW ? left : CW);
+            acc = chan_merge(acc, Stats{n, mean, m2});
+          } else {
+            acc.m2 += m2;
+          }
+        }
+      }
+      st[j].mean = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc.mean), j));
+      st[j].m2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc.m2), j));
+    }
+  }
+
+  const float inv_h = 1.0f / (float)H;
+  float mu[RW], rs[RW];
+#pragma unroll
+  for (int j = 0; j < RW; ++j) {
+    mu[j] = NORM == NT_LAYERNORM ? st[j].mean : 0.0f;
+    rs[j] = 1.0f / sqrtf(st[j].m2 * inv_h + p.eps);
+    const int64_t row = rbase + j;
+    if (slice == 0 && lane == j && row < N) {
+      if (p.rsigma) p.rsigma[row] = rs[j];
+      if constexpr (NORM == NT_LAYERNORM) {
+        if (p.mu) p.mu[row] = mu[j];
+      }
+    }
+  }
+
+  float scale = 1.0f;
+  if constexpr (MODE == MODE_DELAYED) scale = *p.scale;
+  float amax_local = 0.0f;
+  const int valid_rows = (int)(N - rbase < RW ? (N - rbase < 0 ? 0 : N - rbase) : RW);
+  const bool col_aligned = (N % RW) == 0;
+
+  // ---- MXFP8 columnwise block maxima (32 rows = the 4 waves' rows of this band)
+  if constexpr (MXCOL) {
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      float cm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      float gk[8], bk[8];
+      weights(k, gk, bk);
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        float xv[8];
+        strip_to_f32<IN>(xs[j][k], xv);
+        if (j < valid_rows) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float y;
+            if constexpr (NORM == NT_LAYERNORM) y = fmaf((xv[i] - mu[j]) * rs[j], gk[i], bk[i]);
+            else y = (xv[i] * rs[j]) * gk[i];
+            cm[i] = fmaxf(cm[i], fabsf(y));
+          }
+        }
+      }
+      float4 *dst = reinterpret_cast<float4 *>(&colmax[wave][8 * (lane + 64 * k)]);
+      dst[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+      dst[1] = make_float4(cm[4], cm[5], cm[6], cm[7]);
+    }
+    __syncthreads();
+  }
+
+  // ---- outputs, one strip column at a time
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    const int64_t col = cbase + 8 * (lane + 64 * k);
+    float gk[8], bk[8];
+    weights(k, gk, bk);
+    uint2 rcodes[RW];  // rowwise codes (delayed: reused for the columnwise transpose)
+    float colf[8];     // MX columnwise: 2^-X per column
+    int colx[8];
+    if constexpr (MXCOL) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = 8 * (lane + 64 * k) + i;
+        const float a = fmaxf(fmaxf(colmax[0][c], colmax[1][c]), fmaxf(colmax[2][c], colmax[3][c]));
+        colx[i] = mx_exponent(a, fmt);
+        colf[i] = exp2_neg(colx[i]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      const int64_t row = rbase + j;
+      const bool ok = (j < valid_rows) && cv[k];
+      float xv[8], y[8];
+      strip_to_f32<IN>(xs[j][k], xv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (NORM == NT_LAYERNORM) y[i] = fmaf((xv[i] - mu[j]) * rs[j], gk[i], bk[i]);
+        else y[i] = (xv[i] * rs[j]) * gk[i];
+      }
+      if constexpr (MODE == MODE_PLAIN) {
+        if (ok) store_out8(p.y, row * H + col, y, p.out_dtype);
+      } else if constexpr (MODE == MODE_DELAYED) {
+        float u[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          u[i] = y[i] * scale;
+          if (ok) amax_local = fmaxf(amax_local, fabsf(y[i]));
+        }
+        rcodes[j] = fp8_pack8(u, fmt);
+        if (ok && bp.write_row) *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.y) + row * H + col) = rcodes[j];
+      } else {  // MX
+        if (bp.write_row) {
+          float a = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[i]));
+          a = quad_max(ok ? a : 0.0f);
+          const int X = mx_exponent(a, fmt);
+          const float f = exp2_neg(X);
+          float u[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) u[i] = y[i] * f;
+          const uint2 c = fp8_pack8(u, fmt);
+          if (ok) {
+            *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.y) + row * H + col) = c;
+            if ((lane & 3) == 0)
+              static_cast<uint8_t *>(p.scale_inv)[row * p.mx_cols + (col >> 5)] = (uint8_t)(X + 127);
+          }
+        }
+        if constexpr (MXCOL) {
+          float u[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) u[i] = y[i] * colf[i];
+          rcodes[j] = fp8_pack8(u, fmt);
+        }
+      }
+    }
+    if constexpr (COL && MODE != MODE_PLAIN) {
+      if (cv[k] && valid_rows > 0) {
+        uint8_t *colp = static_cast<uint8_t *>(bp.y_col) + col * N + rbase;
+        store_col_codes<RW>(rcodes, colp, N, valid_rows, col_aligned);
+        if constexpr (MXCOL) {
+          if (wave == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              static_cast<uint8_t *>(bp.col_scale_inv)[(col + i) * bp.mx_rows + band] = (uint8_t)(colx[i] + 127);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- end of launch: amax publication and header reset by the last workgroup
+  const bool need_done = (MODE == MODE_DELAYED) || (S > 1);
+  if (need_done) {
+    if constexpr (MODE == MODE_DELAYED) {
+      const float m = wave_max(amax_local);
+      if (lane == 0) max_dev(p.ws + kWsAmax, __float_as_uint(m));
+    }
+    vmem_drain();
+    __syncthreads();
+    if (tid == 0) s_last = add_dev(p.ws + kWsDone, 1u) == gridDim.x - 1 ? 1u : 0u;
+    __syncthreads();
+    if (s_last) {
+      if constexpr (MODE == MODE_DELAYED) {
+        if (tid == 0) {
+          const float tot = __uint_as_float(xchg_dev(p.ws + kWsAmax, 0u));
+          *p.updated_amax = fmaxf(*p.amax_in, tot);
+        }
+      }
+      if (S > 1) {
+        const int64_t used = bp.bands < kWsSlots ? bp.bands : kWsSlots;
+        for (int64_t i = tid; i < used; i += 256) xchg_dev(p.ws + kWsSlot0 + i, 0u);
+        if (tid == 0) xchg_dev(p.ws + kWsTicket, 0u);
+      }
+      vmem_drain();
+      __syncthreads();
+      if (tid == 0) xchg_dev(p.ws + kWsDone, 0u);
+    }
+  }
+  if constexpr (MODE == MODE_DELAYED) {
+    if (band == 0 && slice == 0 && tid == 0) {
+      if (p.scale_inv) *static_cast<float *>(p.scale_inv) = 1.0f / scale;
+      if (bp.col_scale_inv) *static_cast<float *>(bp.col_scale_inv) = 1.0f / scale;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+
+template <int NORM, class IN, int MODE, bool COL>
+static const void *pick_band_cfg(int cfg) {
+  switch (cfg) {
+    case BAND_R8_K1: return (const void *)fwd_band_kernel<NORM, IN, MODE, 8, 1, COL>;
+    case BAND_R8_K2: return (const void *)fwd_band_kernel<NORM, IN, MODE, 8, 2, COL>;
+    case BAND_R4_K2:
+      if constexpr (COL && MODE == MODE_MX) return nullptr;  // MX columnwise blocks need 32-row bands
+      else return (const void *)fwd_band_kernel<NORM, IN, MODE, 4, 2, COL>;
+    case BAND_R1_K4: return COL ? nullptr : (const void *)fwd_band_kernel<NORM, IN, MODE, 1, 4, false>;
+    case BAND_R2_K8: return COL ? nullptr : (const void *)fwd_band_kernel<NORM, IN, MODE, 2, 8, false>;
+    default: return nullptr;
+  }
+}
+
+template <int NORM, class IN>
+static const void *pick_band_mode(int mode, bool col, int cfg) {
+  switch (mode) {
+    case MODE_PLAIN: return col ? nullptr : pick_band_cfg<NORM, IN, MODE_PLAIN, false>(cfg);
+    case MODE_DELAYED:
+      return col ? pick_band_cfg<NORM, IN, MODE_DELAYED, true>(cfg)
+                 : pick_band_cfg<NORM, IN, MODE_DELAYED, false>(cfg);
+    case MODE_MX:
+      return col ? pick_band_cfg<NORM, IN, MODE_MX, true>(cfg) : pick_band_cfg<NORM, IN, MODE_MX, false>(cfg);
+    default: return nullptr;
+  }
+}
+
+template <int NORM>
+static const void *pick_band_in(int in_dtype, int mode, bool col, int cfg) {
+  switch (in_dtype) {
+    case DT_F32: return pick_band_mode<NORM, F32>(mode, col, cfg);
+    case DT_BF16: return pick_band_mode<NORM, BF16>(mode, col, cfg);
+    case DT_F16: return pick_band_mode<NORM, F16>(mode, col, cfg);
+    default: return nullptr;
+  }
+}
+
+const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg) {
+  return norm == NT_LAYERNORM ? pick_band_in<NT_LAYERNORM>(in_dtype, mode, col, cfg)
+                              : pick_band_in<NT_RMSNORM>(in_dtype, mode, col, cfg);
+}
+
+}  // namespace nf8

@@ -1,0 +1,66 @@
+// kernels.hpp -- kernel variants compiled into the library and the lookup functions the host
+// planner uses to obtain them (as `const void*` for hipLaunchKernel / occupancy queries).
+#pragma once
+
+#include "plan.hpp"
+
+namespace nf8 {
+
+// ---- forward row kernel: team of P waves per row, T teams per workgroup, KC strips per lane
+enum RowCfg : int {
+  ROW_W1_K1 = 0,
+  ROW_W1_K2,
+  ROW_W1_K4,
+  ROW_W1_K8,
+  ROW_W4_K2,
+  ROW_W4_K4,
+  ROW_W8_K4,
+  ROW_W2T2_K4,  // 2 waves per row, 2 rows per workgroup
+  ROW_W8_K1,
+  ROW_W4T2_K2,  // 4 waves per row, 2 rows per workgroup
+  ROW_NCFG
+};
+struct RowShape {
+  int P, T, KC;
+  int threads() const { return 64 * P * T; }
+  int64_t cover() const { return 512LL * P * KC; }  // row elements one team holds
+};
+constexpr RowShape kRowShapes[ROW_NCFG] = {{1, 4, 1}, {1, 4, 2}, {1, 4, 4}, {1, 4, 8}, {4, 1, 2},
+                                           {4, 1, 4}, {8, 1, 4}, {2, 2, 4}, {8, 1, 1}, {4, 2, 2}};
+
+// ---- forward band kernel: 4 waves, RW rows per wave, KC strips per lane
+enum BandCfg : int { BAND_R8_K1 = 0, BAND_R8_K2, BAND_R4_K2, BAND_R1_K4, BAND_R2_K8, BAND_NCFG };
+struct BandShape {
+  int RW, KC;
+  bool colwise_ok;
+  int rows() const { return 4 * RW; }
+  int64_t cols() const { return 512LL * KC; }
+};
+constexpr BandShape kBandShapes[BAND_NCFG] = {{8, 1, true}, {8, 2, true}, {4, 2, true}, {1, 4, false}, {2, 8, false}};
+
+// ---- backward: W waves per row, KC strips per lane
+enum BwdCfg : int {
+  BWD_W2_K1 = 0,
+  BWD_W4_K1,
+  BWD_W4_K2,
+  BWD_W8_K2,
+  BWD_W16_K2,
+  BWD_W8_K1,
+  BWD_W16_K1,
+  BWD_W4_K4,
+  BWD_NCFG
+};
+struct BwdShape {
+  int W, KC;
+  int threads() const { return 64 * W; }
+  int64_t cover() const { return 512LL * W * KC; }
+};
+constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1}, {4, 1}, {4, 2}, {8, 2}, {16, 2}, {8, 1}, {16, 1}, {4, 4}};
+
+const void *fwd_row_kernel_ptr(int norm, int in_dtype, int mode, int cfg);
+const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg);
+const void *bwd_kernel_ptr(int norm, int in_dtype, bool add, int cfg);
+const void *bwd_finalize_kernel_ptr();
+const void *ws_init_kernel_ptr();
+
+}  // namespace nf8

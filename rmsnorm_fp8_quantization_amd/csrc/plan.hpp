@@ -1,0 +1,107 @@
+// plan.hpp -- constants, workspace layout and kernel parameter blocks shared by the host
+// launch planner (api.cpp) and the gfx950 kernels.
+//
+// Pages cited: [XLA-Norm] "Implementation: NVIDIA TransformerEngine JAX XLA Normalization";
+// [NVRTC-PR] "Migrate norms and softmax kernels to NVRTC" (TransformerEngine pull request).
+// The pages' dispatch sets grid sizes from device occupancy less an SM margin and keeps
+// barrier and workspace buffers for multi-CTA rows ([NVRTC-PR] Flowchart, Greptile Summary;
+// [XLA-Norm] Description). This file is the MI355X counterpart: one parameter block per
+// kernel family and a fixed workspace header used for cross-workgroup coordination.
+#pragma once
+
+#include <stdint.h>
+
+namespace nf8 {
+
+// element-type codes (identical to norm_dtype_t)
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
+enum : int { NT_LAYERNORM = 0, NT_RMSNORM = 1 };
+// epilogue modes
+enum : int { MODE_PLAIN = 0, MODE_DELAYED = 1, MODE_MX = 2 };
+
+// time limit of a cross-workgroup wait, in ticks of the 100 MHz real-time counter (2 s)
+constexpr uint64_t kSpinLimitTicks = 200000000ull;
+
+// ---- workspace header (NORM_WS_HEADER_BYTES at offset 0 of every workspace) --------------
+// All words are zero between calls. `done` counts finished workgroups; the workgroup that
+// finishes last publishes the per-call results (updated amax) and re-zeroes the header.
+constexpr int kWsHeaderBytes = 16384;
+constexpr int kWsDone = 0;      // u32: finished workgroups of the current launch
+constexpr int kWsTicket = 1;    // u32: band-tile tickets handed out in the current launch
+constexpr int kWsAmax = 2;      // u32: float bits of max |y| of the current launch
+constexpr int kWsError = 3;     // u32: sticky error flags (bit 0: a wait timed out)
+constexpr int kWsSlot0 = 16;    // first band-arrival slot counter
+constexpr int kWsSlots = kWsHeaderBytes / 4 - kWsSlot0;  // 4080 slot counters
+// most workgroups one band may be split over (bounds the LDS used to merge their partials)
+constexpr int kMaxSlices = 64;
+
+// ---- forward row kernel --------------------------------------------------------------------
+// A team of P waves normalises one row at a time; a workgroup holds T teams; each lane owns
+// KC strips of the row (columns 8 * (team_lane + 64 * P * k), k < KC).
+struct FwdRowParams {
+  const void *x;
+  const void *gamma;
+  const void *beta;
+  const float *scale;
+  const float *amax_in;
+  void *y;
+  float *mu;
+  float *rsigma;
+  void *scale_inv;  // delayed: float32[1]; MX: uint8 [rows, ceil(hidden/32)]
+  float *updated_amax;
+  uint32_t *ws;     // workspace header (delayed scaling) or nullptr
+  int64_t rows;
+  int64_t hidden;
+  int64_t mx_cols;  // ceil(hidden / 32)
+  int w_dtype;
+  int out_dtype;    // plain: F32/F16/BF16; delayed / MX: E4M3/E5M2
+  int zero_centered;
+  float eps;
+};
+
+// ---- forward band kernel -------------------------------------------------------------------
+// A workgroup of 4 waves covers a tile of R = 4 * RW rows x CW = 512 * KC columns; wave w owns
+// rows [w * RW, (w + 1) * RW) of the tile and every lane owns KC strips of each of those rows.
+// S workgroups cover one band of R full rows and exchange per-row partial statistics through
+// the workspace. Used for columnwise outputs and for rows too long for one workgroup.
+struct FwdBandParams {
+  FwdRowParams f;        // shared fields (y = rowwise output or nullptr)
+  void *y_col;           // [hidden, rows] columnwise codes or nullptr
+  void *col_scale_inv;   // delayed: float32[1]; MX: uint8 [hidden, ceil(rows/32)]
+  float *partials;       // [bands, S, R, 2] per-row partial statistics (S > 1)
+  int64_t bands;         // ceil(rows / R)
+  int64_t mx_rows;       // ceil(rows / 32)
+  int S;                 // workgroups per band
+  int write_row;         // rowwise output requested
+};
+
+// ---- backward ------------------------------------------------------------------------------
+// A workgroup of W waves handles one row at a time (all lanes of the workgroup on one row),
+// loops over rows g, g + G, ...; lane owns KC strips (columns 8 * (tid + 64 * W * k)).
+// Partial weight gradients of workgroup g go to part[g, :] (and part[G + g, :] for dbeta).
+struct BwdParams {
+  const void *dy;
+  const void *x;
+  const void *residual;  // bwd_add or nullptr
+  const float *mu;
+  const float *rsigma;
+  const void *gamma;
+  void *dx;
+  float *part;           // [G or 2G, hidden]
+  int64_t rows;
+  int64_t hidden;
+  int w_dtype;
+  int zero_centered;
+  int G;
+};
+
+struct FinalizeParams {
+  const float *part;  // [nparts, hidden]
+  void *dgamma;
+  void *dbeta;        // LayerNorm or nullptr
+  int64_t hidden;
+  int G;
+  int w_dtype;
+};
+
+}  // namespace nf8

@@ -1,0 +1,193 @@
+"""Element-wise acceptance checks of GPU outputs against the CPU oracle.
+
+Tolerances (written here, used by every parity test):
+  mu              |g - v| / max(|v|, 1e-3 * sigma_row) <= 1e-5
+  rsigma          |g - v| / v <= 1e-5
+  bf16 / f16 y    ordered-bit distance to the nearest-even rounding of v <= 1 ulp (where
+                  LayerNorm's xhat*g + beta cancels: within half an ulp plus the binary32
+                  evaluation bound 2^-21 * (|xhat*g| + |beta|))
+  f32 y, f32 dx   |g - v| / max(|v|, rms_row(v)) <= 1e-5
+  FP8 codes       ordered code distance <= 1; at most 0.1% of elements differ; each
+                  differing element's exact scaled value lies within 1e-5 (relative) of
+                  the midpoint between the two codes' values, i.e. on a rounding boundary
+  E8M0 scales     bit-exact, except blocks whose float64 maximum lies within 2^-21
+                  (relative) of a power of two, where the binary32 maximum may fall on
+                  either side: there either neighbouring exponent is accepted and the
+                  block's codes are checked under the GPU's exponent
+  amax            |g - v| / v <= 1e-6
+  scale_inv       bit-exact
+  bf16 / f16 dx   (|g - v| - half_ulp(v)) / max(|v|, rms_row(v)) <= 2e-3: the error beyond
+                  the output's own nearest rounding (bf16 alone can be 2^-8 relative away
+                  from v just above a power of two, more than 2e-3)
+  dgamma, dbeta   |g - v| / max(|v|, rms(v)) <= 1e-4
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from oracle import formats as F
+
+TOL = dict(mu=1e-5, rsigma=1e-5, f32=1e-5, dx16=2e-3, wgrad=1e-4, amax=1e-6, fp8_frac=1e-3,
+           fp8_tau=1e-5, e8m0_window=2.0 ** -21)
+
+
+class Report(dict):
+    """Counts kept by a check (printed by tests on failure)."""
+
+
+def _ordered(bits: np.ndarray, nbits: int) -> np.ndarray:
+    """Map sign-magnitude float bit patterns to integers ordered like the values."""
+    b = bits.astype(np.int64)
+    sign = 1 << (nbits - 1)
+    mag = b & (sign - 1)
+    return np.where(b & sign, -mag, mag)
+
+
+def check_stats(mu_g, rs_g, mu_ref, rs_ref, rows_sigma=None):
+    rs_g = np.asarray(rs_g, np.float64)
+    err = np.abs(rs_g - rs_ref) / rs_ref
+    assert np.all(err <= TOL["rsigma"]), f"rsigma max rel err {err.max():.3e}"
+    if mu_ref is not None:
+        sig = rows_sigma if rows_sigma is not None else 1.0 / rs_ref
+        den = np.maximum(np.abs(mu_ref), 1e-3 * sig)
+        e2 = np.abs(np.asarray(mu_g, np.float64) - mu_ref) / den
+        assert np.all(e2 <= TOL["mu"]), f"mu max rel err {e2.max():.3e}"
+
+
+def check_hp(y_g: np.ndarray, v: np.ndarray, dtype: str, what="y", terms=None):
+    """High-precision output (f32 / f16 / bf16 storage) against unrounded v.
+
+    16-bit outputs: at most 1 ulp from the nearest-even rounding of v. Where y is the small
+    difference of larger terms (LayerNorm: xhat * g + beta cancelling; `terms` holds
+    |xhat * g| + |beta|), a binary32 evaluation is only accurate to a few binary32 ulps of
+    those terms, which can exceed one ulp of the small result: such elements pass when
+    |g - v| <= half an ulp of v + 2^-21 * terms (eight binary32 roundings of the terms)."""
+    if dtype == "f32":
+        g = np.asarray(y_g, np.float64)
+        rms = np.sqrt(np.mean(v * v, axis=-1, keepdims=True))
+        den = np.maximum(np.abs(v), rms)
+        err = np.abs(g - v) / np.where(den > 0, den, 1.0)
+        assert np.all(err <= TOL["f32"]), f"{what}: max rel err {err.max():.3e}"
+        return Report(max_err=float(err.max()))
+    ref = oracle.encode_storage(v, dtype)
+    raw = np.asarray(y_g).view(np.uint16)
+    d = np.abs(_ordered(raw, 16) - _ordered(np.asarray(ref).view(np.uint16), 16))
+    far = d > 1
+    n_cancel = 0
+    if far.any() and terms is not None:
+        g = F.decode_storage(raw if dtype == "bf16" else raw.view(np.float16), dtype)
+        bound = half_ulp(v, dtype) + 2.0 ** -21 * np.asarray(terms, np.float64)
+        ok = np.abs(g - v) <= bound
+        n_cancel = int((far & ok).sum())
+        far = far & ~ok
+    assert not far.any(), f"{what}: {int(far.sum())} elements more than 1 ulp off"
+    return Report(off_by_one=int((d == 1).sum()), cancellation=n_cancel)
+
+
+def check_fp8(codes_g: np.ndarray, codes_ref: np.ndarray, u_exact: np.ndarray, fp8: str, what="codes"):
+    """FP8 codes: <= 1 code apart, <= 0.1 % differing, every difference on a rounding boundary."""
+    fmt = F.FORMATS[fp8]
+    cg = np.asarray(codes_g, np.uint8)
+    cr = np.asarray(codes_ref, np.uint8)
+    diff = cg != cr
+    n = int(diff.sum())
+    if n == 0:
+        return Report(differ=0)
+    og = _ordered(cg.astype(np.int64), 8)
+    orf = _ordered(cr.astype(np.int64), 8)
+    dist = np.abs(og - orf)
+    # +0 / -0 are the same value
+    zero_pair = (F.fp8_decode(cg[diff], fmt) == 0) & (F.fp8_decode(cr[diff], fmt) == 0)
+    assert np.all((dist[diff] <= 1) | zero_pair), f"{what}: codes more than one step apart"
+    frac = n / cg.size
+    assert frac <= TOL["fp8_frac"], f"{what}: {n} of {cg.size} codes differ ({frac:.2e})"
+    vg = F.fp8_decode(cg[diff], fmt)
+    vr = F.fp8_decode(cr[diff], fmt)
+    mid = 0.5 * (vg + vr)
+    u = np.clip(np.asarray(u_exact, np.float64)[diff], -fmt.max_finite, fmt.max_finite)
+    ok = (np.abs(u - mid) <= TOL["fp8_tau"] * np.maximum(np.abs(u), 2.0 ** (fmt.emin - fmt.mant_bits))) | zero_pair
+    assert np.all(ok), f"{what}: {int((~ok).sum())} differing codes not on a rounding boundary"
+    return Report(differ=n)
+
+
+def check_delayed(out, v, scale, amax_in, fp8, rowwise=True, colwise=False):
+    """All delayed-scaling outputs against the oracle (v: float64 values [rows, hidden])."""
+    ref = oracle.delayed_epilogue(v, scale, amax_in, fp8, colwise)
+    u = v * np.float64(np.float32(scale))
+    rep = Report()
+    if rowwise:
+        rep["row"] = check_fp8(out["y"], ref["rowwise"], u, fp8, "rowwise codes")
+        assert np.float32(out["scale_inv"]).view(np.uint32) == np.float32(ref["scale_inv"]).view(np.uint32)
+    if colwise:
+        rep["col"] = check_fp8(out["y_colwise"], ref["colwise"], np.ascontiguousarray(u.T), fp8, "colwise codes")
+        assert np.float32(out["colwise_scale_inv"]).view(np.uint32) == np.float32(ref["scale_inv"]).view(np.uint32)
+    a = float(out["amax"])
+    assert abs(a - ref["amax"]) <= TOL["amax"] * ref["amax"], f"amax {a} vs {ref['amax']}"
+    return rep
+
+
+def check_mx_rows(codes_g, scales_g, v, fp8, what="mx"):
+    """MXFP8 blocks along the last axis of v (float64 [r, c]) against GPU codes / scale bytes."""
+    fmt = F.FORMATS[fp8]
+    v = np.asarray(v, np.float64)
+    r, c = v.shape
+    nb = -(-c // 32)
+    y32 = F.to_f32(v)
+    codes_g = np.asarray(codes_g, np.uint8)
+    scales_g = np.asarray(scales_g, np.uint8)
+    assert scales_g.shape == (r, nb) and codes_g.shape == (r, c)
+    boundary = 0
+    code_rep = []
+    for b in range(nb):
+        sl = slice(32 * b, min(32 * b + 32, c))
+        blk32 = y32[:, sl]
+        a64 = np.max(np.abs(v[:, sl]), axis=1)
+        x_ref = F.e8m0_exponent(np.max(np.abs(blk32), axis=1), fp8)
+        x_g = scales_g[:, b].astype(np.int64) - 127
+        bad = x_g != x_ref
+        if bad.any():
+            # allowed only next to a power of two, and only by one step
+            k = np.floor(np.log2(np.where(a64 > 0, a64, 1.0)))
+            near = (np.abs(a64 - 2.0 ** k) <= TOL["e8m0_window"] * a64) | \
+                   (np.abs(a64 - 2.0 ** (k + 1)) <= TOL["e8m0_window"] * a64)
+            assert np.all(near[bad] & (np.abs(x_g - x_ref)[bad] == 1)), \
+                f"{what}: {int(bad.sum())} E8M0 scales differ away from a power-of-two boundary"
+            boundary += int(bad.sum())
+        scaled = blk32 * np.ldexp(1.0, -x_g)[:, None]
+        ref_codes = F.fp8_quantize(F.round_nearest_even(scaled, F.FP32), fmt)
+        u_exact = v[:, sl] * np.ldexp(1.0, -x_g)[:, None]
+        code_rep.append(ref_codes)
+        check_fp8(codes_g[:, sl], ref_codes, u_exact, fp8, f"{what} block {b}")
+    return Report(boundary_blocks=boundary)
+
+
+def half_ulp(v, dtype):
+    """Half the spacing of the storage format around each |v| (the output rounding bound)."""
+    fmt = F.FORMATS[dtype]
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.where(a > 0, F.floor_log2(np.where(a > 0, a, 1.0)), fmt.emin)
+    return np.ldexp(0.5, (np.maximum(e, fmt.emin) - fmt.mant_bits).astype(np.int64))
+
+
+def check_dx(dx_g, v, dtype):
+    """dx against unrounded v: the error beyond the output's own nearest rounding (half an
+    ulp of the storage format) must stay within the relative tolerance."""
+    g = np.asarray(dx_g, np.float64) if dtype == "f32" else F.decode_storage(np.asarray(dx_g), dtype)
+    rms = np.sqrt(np.mean(v * v, axis=-1, keepdims=True))
+    den = np.maximum(np.abs(v), rms)
+    excess = np.maximum(np.abs(g - v) - half_ulp(v, dtype), 0.0)
+    err = excess / np.where(den > 0, den, 1.0)
+    tol = TOL["f32"] if dtype == "f32" else TOL["dx16"]
+    assert np.all(err <= tol), f"dx: max rel err beyond output rounding {err.max():.3e} (tol {tol})"
+    return Report(max_err=float(err.max()))
+
+
+def check_wgrad(g_gpu, v, dtype="f32", what="dgamma"):
+    g = np.asarray(g_gpu, np.float64) if dtype == "f32" else F.decode_storage(np.asarray(g_gpu), dtype)
+    rms = np.sqrt(np.mean(v * v))
+    den = np.maximum(np.abs(v), rms if rms > 0 else 1.0)
+    err = np.abs(g - v) / den
+    tol = TOL["wgrad"] if dtype == "f32" else 2 ** -8
+    assert np.all(err <= tol), f"{what}: max rel err {err.max():.3e}"
+    return Report(max_err=float(err.max()))

@@ -1,0 +1,208 @@
+"""Host-side tests of the C ABI (no GPU): symbols, workspace queries, argument validation.
+
+Every call here either is a pure query or fails validation, which the library performs
+before it touches the HIP runtime, so nothing is enqueued and no device is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "normfp8.h")
+
+L = pytest.importorskip("rmsnorm_fp8_quantization_amd._lib")
+
+
+def _lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libnormfp8.so not built (run __graft_entry__.build())")
+    return L.load()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(norm_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    fns = header_functions()
+    assert set(fns) == set(L.EXPORTS), fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.norm_abi_version() == 1
+
+
+def test_enum_values_match_header():
+    src = open(HEADER).read()
+    for name in ("NORM_OK", "NORM_ERR_INVALID_ARG", "NORM_ERR_UNSUPPORTED", "NORM_ERR_MISALIGNED",
+                 "NORM_ERR_WORKSPACE_TOO_SMALL", "NORM_ERR_HIP", "NORM_LAYERNORM", "NORM_RMSNORM",
+                 "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_FP8_E4M3", "NORM_FP8_E5M2",
+                 "NORM_SCALING_NONE", "NORM_SCALING_DELAYED_TENSOR", "NORM_SCALING_MXFP8_1D32",
+                 "NORM_Q_ROWWISE", "NORM_Q_COLWISE", "NORM_Q_ROWWISE_COLWISE"):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
+        assert m and int(m.group(1)) == getattr(L, name), name
+    m = re.search(r"#define NORM_WS_HEADER_BYTES (\d+)", src)
+    assert int(m.group(1)) == L.NORM_WS_HEADER_BYTES
+
+
+def fwd_ws(rows, hidden, in_dt=L.NORM_BF16, w=L.NORM_F32, out=L.NORM_BF16, norm=L.NORM_RMSNORM,
+           scaling=L.NORM_SCALING_NONE, layout=L.NORM_Q_ROWWISE):
+    _lib()
+    n = ctypes.c_size_t(12345)
+    rc = L.status("norm_fwd_workspace_size", rows, hidden, in_dt, w, out, norm, scaling, layout, 0, 1e-5,
+                  0, 1, ctypes.byref(n))
+    return rc, n.value
+
+
+def bwd_ws(rows, hidden, norm=L.NORM_LAYERNORM, add=0, in_dt=L.NORM_BF16):
+    _lib()
+    n = ctypes.c_size_t(12345)
+    rc = L.status("norm_bwd_workspace_size", rows, hidden, in_dt, L.NORM_F32, norm, 0, 1e-5, 0, add,
+                  ctypes.byref(n))
+    return rc, n.value
+
+
+def test_fwd_workspace_queries():
+    assert fwd_ws(16384, 4096) == (L.NORM_OK, 0)                     # row path: no workspace
+    rc, n = fwd_ws(32768, 8192, out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_DELAYED_TENSOR,
+                   layout=L.NORM_Q_ROWWISE_COLWISE)
+    assert rc == L.NORM_OK and n > L.NORM_WS_HEADER_BYTES             # header + band partials
+    rc, n2 = fwd_ws(32768, 8192, out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_DELAYED_TENSOR)
+    assert rc == L.NORM_OK and n2 == L.NORM_WS_HEADER_BYTES           # amax needs the header only
+    rc, n3 = fwd_ws(1024, 65536, norm=L.NORM_LAYERNORM)               # long rows: split path
+    assert rc == L.NORM_OK and n3 > L.NORM_WS_HEADER_BYTES
+    # deterministic and monotone in rows
+    assert fwd_ws(1024, 65536, norm=L.NORM_LAYERNORM) == (rc, n3)
+    assert fwd_ws(2048, 65536, norm=L.NORM_LAYERNORM)[1] >= n3
+    # rows == 0 is valid
+    assert fwd_ws(0, 4096)[0] == L.NORM_OK
+
+
+def test_bwd_workspace_queries():
+    rc, n = bwd_ws(16384, 4096)
+    assert rc == L.NORM_OK and n >= L.NORM_WS_HEADER_BYTES + 4096 * 4 * 2
+    rc1, n1 = bwd_ws(16384, 4096, norm=L.NORM_RMSNORM)
+    assert rc1 == L.NORM_OK and n1 < n                                 # no dbeta partials
+    assert bwd_ws(32768, 8192, norm=L.NORM_RMSNORM, add=1)[0] == L.NORM_OK
+    assert bwd_ws(32768, 8192, norm=L.NORM_LAYERNORM, add=1)[0] == L.NORM_ERR_INVALID_ARG
+    assert bwd_ws(10, 4096)[1] <= n                                    # monotone in rows
+    assert bwd_ws(16, 1 << 20)[0] == L.NORM_ERR_UNSUPPORTED            # beyond this build's backward
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=100), L.NORM_ERR_UNSUPPORTED),                        # not a multiple of 8
+    (dict(hidden=0), L.NORM_ERR_INVALID_ARG),
+    (dict(rows=-1), L.NORM_ERR_INVALID_ARG),
+    (dict(norm=7), L.NORM_ERR_INVALID_ARG),
+    (dict(in_dt=L.NORM_FP8_E4M3), L.NORM_ERR_UNSUPPORTED),
+    (dict(out=L.NORM_FP8_E4M3), L.NORM_ERR_UNSUPPORTED),               # FP8 out without scaling
+    (dict(scaling=L.NORM_SCALING_DELAYED_TENSOR), L.NORM_ERR_UNSUPPORTED),  # bf16 out with scaling
+    (dict(scaling=9), L.NORM_ERR_INVALID_ARG),
+    (dict(layout=L.NORM_Q_ROWWISE_COLWISE), L.NORM_ERR_UNSUPPORTED),   # colwise without FP8
+    (dict(layout=0), L.NORM_ERR_INVALID_ARG),
+])
+def test_fwd_workspace_query_rejects(kw, code):
+    args = dict(rows=16, hidden=64)
+    args.update(kw)
+    assert fwd_ws(**args)[0] == code
+
+
+FAKE = 1 << 20        # aligned fake device addresses: never dereferenced, validation fails first
+
+
+def _fwd(**kw):
+    _lib()
+    a = dict(stream=None, x=FAKE, gamma=FAKE, beta=None, scale=None, amax=None, y=FAKE, y_col=None,
+             mu=None, rs=FAKE, si=None, csi=None, upd=None, ws=None, wsb=0, rows=16, hidden=64,
+             in_dt=L.NORM_BF16, w=L.NORM_F32, out=L.NORM_BF16, norm=L.NORM_RMSNORM,
+             scaling=L.NORM_SCALING_NONE, layout=L.NORM_Q_ROWWISE, zc=0, eps=1e-5, margin=0)
+    a.update(kw)
+    return L.status("norm_fwd", a["stream"], a["x"], a["gamma"], a["beta"], a["scale"], a["amax"], a["y"],
+                    a["y_col"], a["mu"], a["rs"], a["si"], a["csi"], a["upd"], a["ws"], a["wsb"], a["rows"],
+                    a["hidden"], a["in_dt"], a["w"], a["out"], a["norm"], a["scaling"], a["layout"], a["zc"],
+                    a["eps"], a["margin"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), L.NORM_ERR_INVALID_ARG),
+    (dict(gamma=None), L.NORM_ERR_INVALID_ARG),
+    (dict(y=None), L.NORM_ERR_INVALID_ARG),
+    (dict(beta=FAKE), L.NORM_ERR_INVALID_ARG),                                 # beta with RMSNorm
+    (dict(norm=L.NORM_LAYERNORM), L.NORM_ERR_INVALID_ARG),                     # LayerNorm without beta
+    (dict(x=FAKE + 4), L.NORM_ERR_MISALIGNED),
+    (dict(y=FAKE + 8), L.NORM_ERR_MISALIGNED),
+    (dict(hidden=60), L.NORM_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), L.NORM_ERR_INVALID_ARG),
+    (dict(margin=-1), L.NORM_ERR_INVALID_ARG),
+    (dict(y_col=FAKE), L.NORM_ERR_INVALID_ARG),                                # colwise buffer, rowwise layout
+    # delayed scaling without its scalars / workspace
+    (dict(out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_DELAYED_TENSOR), L.NORM_ERR_INVALID_ARG),
+    (dict(out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_DELAYED_TENSOR, scale=FAKE, amax=FAKE, upd=FAKE,
+          si=FAKE), L.NORM_ERR_INVALID_ARG),                                   # workspace NULL
+    (dict(out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_DELAYED_TENSOR, scale=FAKE, amax=FAKE, upd=FAKE,
+          si=FAKE, ws=FAKE, wsb=100), L.NORM_ERR_WORKSPACE_TOO_SMALL),
+    (dict(out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_MXFP8_1D32), L.NORM_ERR_INVALID_ARG),  # no scale_inv
+    (dict(out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_MXFP8_1D32, si=FAKE,
+          layout=L.NORM_Q_ROWWISE_COLWISE), L.NORM_ERR_INVALID_ARG),           # no y_colwise
+    (dict(out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_MXFP8_1D32, y_col=FAKE, csi=FAKE,
+          layout=L.NORM_Q_COLWISE), L.NORM_ERR_INVALID_ARG),                   # rowwise y given, colwise-only
+])
+def test_fwd_rejects_before_enqueue(kw, code):
+    rc = _fwd(**kw)
+    assert rc == code, L.load().norm_last_error()
+    assert L.load().norm_last_error()
+
+
+def _bwd(**kw):
+    _lib()
+    a = dict(stream=None, dy=FAKE, x=FAKE, mu=FAKE, rs=FAKE, gamma=FAKE, dx=FAKE, dg=FAKE, db=FAKE, ws=FAKE,
+             wsb=1 << 30, rows=16, hidden=64, in_dt=L.NORM_BF16, w=L.NORM_F32, norm=L.NORM_LAYERNORM,
+             zc=0, margin=0)
+    a.update(kw)
+    return L.status("norm_bwd", a["stream"], a["dy"], a["x"], a["mu"], a["rs"], a["gamma"], a["dx"], a["dg"],
+                    a["db"], a["ws"], a["wsb"], a["rows"], a["hidden"], a["in_dt"], a["w"], a["norm"], a["zc"],
+                    a["margin"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dy=None), L.NORM_ERR_INVALID_ARG),
+    (dict(mu=None), L.NORM_ERR_INVALID_ARG),
+    (dict(db=None), L.NORM_ERR_INVALID_ARG),
+    (dict(norm=L.NORM_RMSNORM), L.NORM_ERR_INVALID_ARG),          # dbeta given for RMSNorm
+    (dict(ws=None), L.NORM_ERR_INVALID_ARG),
+    (dict(wsb=1000), L.NORM_ERR_WORKSPACE_TOO_SMALL),
+    (dict(dx=FAKE + 2), L.NORM_ERR_MISALIGNED),
+    (dict(hidden=12), L.NORM_ERR_UNSUPPORTED),
+    (dict(hidden=1 << 20), L.NORM_ERR_UNSUPPORTED),
+])
+def test_bwd_rejects_before_enqueue(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_bwd_add_requires_residual():
+    _lib()
+    rc = L.status("norm_bwd_add", None, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 16, 64,
+                  L.NORM_BF16, L.NORM_F32, 0, 0)
+    assert rc == L.NORM_ERR_INVALID_ARG
+
+
+def test_workspace_init_rejects_small_or_null():
+    _lib()
+    assert L.status("norm_workspace_init", None, None, 1 << 20) == L.NORM_ERR_INVALID_ARG
+    assert L.status("norm_workspace_init", None, FAKE, 100) == L.NORM_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import importlib
+    mod = importlib.import_module("rmsnorm_fp8_quantization_amd._lib")
+    monkeypatch.setattr(mod, "_lib", None)
+    monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        mod.load()

@@ -1,0 +1,322 @@
+"""GPU parity: the HIP library (called through its C ABI via the binding) against the CPU oracle.
+
+Inputs are seeded synthetic tensors from ``workloads``; the same host arrays feed both sides.
+Shapes span several tiles and ragged tails; every forward layout (wave / workgroup team,
+band split, columnwise band) is forced on small shapes through the planner's override knobs.
+Tolerances are those of tests/checks.py.
+"""
+import contextlib
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import formats as F
+import checks
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import rmsnorm_fp8_quantization_amd as nf  # noqa: E402
+
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+EPS = 1e-5
+
+
+@contextlib.contextmanager
+def env(**kv):
+    old = {k: os.environ.get(k) for k in kv}
+    try:
+        for k, v in kv.items():
+            os.environ[k] = str(v)
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def bits(t):
+    return workloads.to_numpy_bits(t.cpu())
+
+
+def host_np(t, dtype):
+    """Stored values of a host tensor as the oracle's storage arrays."""
+    return workloads.to_numpy_bits(t)
+
+
+def oracle_fwd(case, norm, in_dt, w_dt, zc):
+    return oracle.forward_stored(host_np(case["x"], in_dt), host_np(case["gamma"], w_dt),
+                                 host_np(case["beta"], w_dt) if norm == "layernorm" else None,
+                                 norm=norm, eps=EPS, in_dtype=in_dt, w_dtype=w_dt, zero_centered_gamma=zc)
+
+
+def ln_terms(case, ref, norm, w_dt="f32"):
+    """|xhat * g| + |beta| per element (LayerNorm), the magnitude of the summed terms."""
+    if norm != "layernorm":
+        return None
+    beta = F.decode_storage(host_np(case["beta"], w_dt), w_dt)[None, :]
+    return np.abs(ref["v"] - beta) + np.abs(beta)
+
+
+def gpu(case, *names):
+    return [case[n].cuda() if n in case else None for n in names]
+
+
+def assert_ws_clean():
+    torch.cuda.synchronize()
+    assert nf.workspace_check() == 0
+
+
+# ------------------------------------------------------------------------------ plain forward
+
+PLAIN_SHAPES = [(1, 8), (3, 200), (37, 1024), (64, 4096), (5, 4104), (7, 8192), (3, 16384), (2, 20480),
+                (4, 65536), (300, 512)]
+
+
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("in_dt", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("rows,hidden", PLAIN_SHAPES)
+def test_fwd_plain(norm, in_dt, rows, hidden):
+    case = workloads.small_case(norm, rows, hidden, in_dt, "f32", seed=rows + hidden)
+    ref = oracle_fwd(case, norm, in_dt, "f32", False)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    out = nf.fwd(x, g, b, norm=norm, eps=EPS)
+    checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
+                       out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+    checks.check_hp(bits(out["y"]), ref["v"], in_dt, terms=ln_terms(case, ref, norm))
+
+
+@pytest.mark.parametrize("out_dt", ["f32", "f16"])
+def test_fwd_plain_other_out_dtype_and_bf16_weights(out_dt):
+    case = workloads.small_case("layernorm", 33, 3000 - 3000 % 8, "bf16", "bf16", seed=3)
+    ref = oracle_fwd(case, "layernorm", "bf16", "bf16", False)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    out = nf.fwd(x, g, b, norm="layernorm", eps=EPS, out_dtype=TDT[out_dt])
+    checks.check_hp(bits(out["y"]), ref["v"], out_dt, terms=ln_terms(case, ref, "layernorm", "bf16"))
+
+
+ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096]   # per row layout
+BWD_COVER = [1024, 2048, 4096, 8192, 16384, 4096, 8192, 8192]
+
+
+@pytest.mark.parametrize("cfg", range(len(ROW_COVER)))
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+def test_fwd_every_row_layout(cfg, norm):
+    hidden = ROW_COVER[cfg] - 8   # ragged: the last strip of the row is masked
+    rows = 19
+    case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=cfg)
+    ref = oracle_fwd(case, norm, "bf16", "f32", False)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    with env(NORMFP8_ROW_CFG=cfg):
+        out = nf.fwd(x, g, b, norm=norm, eps=EPS)
+    checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
+                       out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+    checks.check_hp(bits(out["y"]), ref["v"], "bf16", terms=ln_terms(case, ref, norm))
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("rows,hidden", [(37, 1000), (9, 12288)])
+def test_fwd_forced_band_split(cfg, norm, rows, hidden):
+    case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=cfg + 50)
+    ref = oracle_fwd(case, norm, "bf16", "f32", False)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    with env(NORMFP8_FORCE_BAND=1, NORMFP8_BAND_CFG=cfg):
+        out = nf.fwd(x, g, b, norm=norm, eps=EPS)
+    checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
+                       out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+    checks.check_hp(bits(out["y"]), ref["v"], "bf16", terms=ln_terms(case, ref, norm))
+    assert_ws_clean()
+
+
+def test_fwd_zero_centered_gamma_and_zero_rows():
+    case = workloads.small_case("rmsnorm", 11, 768, "bf16", "f32", seed=9, zero_centered_gamma=True)
+    ref = oracle_fwd(case, "rmsnorm", "bf16", "f32", True)
+    x, g = gpu(case, "x", "gamma")
+    out = nf.fwd(x, g, None, norm="rmsnorm", eps=EPS, zero_centered_gamma=True)
+    checks.check_hp(bits(out["y"]), ref["v"], "bf16")
+    empty = nf.fwd(x[:0], g, None, norm="rmsnorm", eps=EPS)
+    assert empty["y"].shape == (0, 768)
+
+
+# ------------------------------------------------------------------------------ delayed scaling
+
+@pytest.mark.parametrize("fp8", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("layout", ["rowwise", "rowwise_colwise", "colwise"])
+@pytest.mark.parametrize("norm,rows,hidden", [("rmsnorm", 64, 1024), ("rmsnorm", 45, 4104),
+                                              ("layernorm", 100, 2048), ("rmsnorm", 33, 20480)])
+def test_fwd_delayed(fp8, layout, norm, rows, hidden):
+    case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=rows)
+    xh = case["x"].float()
+    xh[::7, ::13] *= 20.0                       # outliers beyond the scale's range
+    case["x"] = xh.to(torch.bfloat16)
+    ref = oracle_fwd(case, norm, "bf16", "f32", False)
+    scale = float(np.float32(F.E4M3.max_finite if fp8 == "e4m3" else F.E5M2.max_finite) /
+                  np.float32(np.max(np.abs(ref["v"])) / 4))
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    st = torch.tensor([scale], dtype=torch.float32, device="cuda")
+    am = torch.tensor([0.25], dtype=torch.float32, device="cuda")
+    out = nf.fwd(x, g, b, norm=norm, eps=EPS, scaling="delayed", fp8=fp8, scale=st, amax=am, layout=layout)
+    got = {"y": bits(out["y"]) if out["y"] is not None else None,
+           "y_colwise": bits(out["y_colwise"]) if out["y_colwise"] is not None else None,
+           "scale_inv": out["scale_inv"].item() if out["scale_inv"] is not None else None,
+           "colwise_scale_inv": out["colwise_scale_inv"].item() if out["colwise_scale_inv"] is not None else None,
+           "amax": out["amax"].item()}
+    checks.check_delayed(got, ref["v"], scale, 0.25, fp8, rowwise=layout != "colwise",
+                         colwise=layout != "rowwise")
+    checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
+                       out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+    assert_ws_clean()
+
+
+def test_fwd_delayed_amax_inplace_and_accumulates():
+    case = workloads.small_case("rmsnorm", 16, 512, "bf16", "f32", seed=2)
+    ref = oracle_fwd(case, "rmsnorm", "bf16", "f32", False)
+    x, g = gpu(case, "x", "gamma")
+    st = torch.tensor([100.0], device="cuda")
+    am = torch.tensor([1e4], device="cuda")          # larger than max |y|: kept
+    out = nf.fwd(x, g, None, norm="rmsnorm", scaling="delayed", scale=st, amax=am, amax_inplace=True)
+    torch.cuda.synchronize()
+    assert out["amax"].data_ptr() == am.data_ptr() and am.item() == 1e4
+    am.zero_()
+    nf.fwd(x, g, None, norm="rmsnorm", scaling="delayed", scale=st, amax=am, amax_inplace=True)
+    assert abs(am.item() - np.max(np.abs(ref["v"]))) <= 1e-6 * np.max(np.abs(ref["v"]))
+    assert_ws_clean()
+
+
+# ------------------------------------------------------------------------------ MXFP8
+
+@pytest.mark.parametrize("fp8", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("layout", ["rowwise", "rowwise_colwise", "colwise"])
+@pytest.mark.parametrize("norm,rows,hidden,zc", [("rmsnorm", 64, 1024, True), ("rmsnorm", 45, 1000, False),
+                                                 ("layernorm", 96, 4096, False), ("rmsnorm", 32, 12288, True),
+                                                 ("rmsnorm", 7, 512, False)])
+def test_fwd_mxfp8(fp8, layout, norm, rows, hidden, zc):
+    case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=hidden + rows, zero_centered_gamma=zc)
+    ref = oracle_fwd(case, norm, "bf16", "f32", zc)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    out = nf.fwd(x, g, b, norm=norm, eps=EPS, zero_centered_gamma=zc, scaling="mxfp8", fp8=fp8, layout=layout)
+    if layout != "colwise":
+        checks.check_mx_rows(bits(out["y"]), bits(out["scale_inv"]), ref["v"], fp8, "mx rowwise")
+    if layout != "rowwise":
+        checks.check_mx_rows(bits(out["y_colwise"]), bits(out["colwise_scale_inv"]),
+                             np.ascontiguousarray(ref["v"].T), fp8, "mx colwise")
+    checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
+                       out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+    assert_ws_clean()
+
+
+def test_fwd_mxfp8_zero_block():
+    case = workloads.small_case("layernorm", 32, 256, "bf16", "f32", seed=4)
+    case["gamma"][:32] = 0.0                          # first column block of every row is 0 * x + beta
+    case["beta"][:32] = 0.0
+    ref = oracle_fwd(case, "layernorm", "bf16", "f32", False)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    out = nf.fwd(x, g, b, norm="layernorm", scaling="mxfp8", layout="rowwise_colwise")
+    sc = bits(out["scale_inv"])
+    assert np.all(sc[:, 0] == 0) and np.all(bits(out["y"])[:, :32] == 0)
+    checks.check_mx_rows(bits(out["y_colwise"]), bits(out["colwise_scale_inv"]),
+                         np.ascontiguousarray(ref["v"].T), "e4m3", "mx colwise")
+
+
+# ------------------------------------------------------------------------------ backward
+
+def oracle_bwd(case, norm, in_dt, w_dt, zc, ref_fwd, add=False):
+    return oracle.backward_stored(host_np(case["dy"], in_dt), host_np(case["x"], in_dt),
+                                  ref_fwd["mu"], ref_fwd["rsigma"], host_np(case["gamma"], w_dt),
+                                  norm=norm, in_dtype=in_dt, w_dtype=w_dt, zero_centered_gamma=zc,
+                                  residual_dy=host_np(case["residual_dy"], in_dt) if add else None)
+
+
+BWD_SHAPES = [(1, 8), (7, 1000), (64, 1024), (300, 2048), (33, 4096), (129, 8192), (5, 16384)]
+
+
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,hidden", BWD_SHAPES)
+def test_bwd(norm, in_dt, rows, hidden):
+    case = workloads.small_case(norm, rows, hidden, in_dt, "f32", seed=rows * 3 + hidden)
+    ref_f = oracle_fwd(case, norm, in_dt, "f32", False)
+    ref = oracle_bwd(case, norm, in_dt, "f32", False, ref_f)
+    dy, x, g = gpu(case, "dy", "x", "gamma")
+    mu = torch.tensor(ref_f["mu"], dtype=torch.float32, device="cuda") if norm == "layernorm" else None
+    rs = torch.tensor(ref_f["rsigma"], dtype=torch.float32, device="cuda")
+    out = nf.bwd(dy, x, mu, rs, g, norm=norm)
+    checks.check_dx(bits(out["dx"]), ref["dx"], in_dt)
+    checks.check_wgrad(out["dgamma"].cpu().numpy(), ref["dgamma"])
+    if norm == "layernorm":
+        checks.check_wgrad(out["dbeta"].cpu().numpy(), ref["dbeta"], what="dbeta")
+
+
+@pytest.mark.parametrize("cfg", range(len(BWD_COVER)))
+def test_bwd_every_layout(cfg):
+    hidden = BWD_COVER[cfg] - 8
+    case = workloads.small_case("layernorm", 21, hidden, "bf16", "f32", seed=cfg + 5)
+    ref_f = oracle_fwd(case, "layernorm", "bf16", "f32", False)
+    ref = oracle_bwd(case, "layernorm", "bf16", "f32", False, ref_f)
+    dy, x, g = gpu(case, "dy", "x", "gamma")
+    mu = torch.tensor(ref_f["mu"], dtype=torch.float32, device="cuda")
+    rs = torch.tensor(ref_f["rsigma"], dtype=torch.float32, device="cuda")
+    with env(NORMFP8_BWD_CFG=cfg):
+        out = nf.bwd(dy, x, mu, rs, g, norm="layernorm")
+    checks.check_dx(bits(out["dx"]), ref["dx"], "bf16")
+    checks.check_wgrad(out["dgamma"].cpu().numpy(), ref["dgamma"])
+    checks.check_wgrad(out["dbeta"].cpu().numpy(), ref["dbeta"], what="dbeta")
+
+
+@pytest.mark.parametrize("rows,hidden,zc", [(1, 8, False), (77, 2048, True), (256, 8192, False)])
+def test_bwd_add(rows, hidden, zc):
+    case = workloads.small_case("rmsnorm", rows, hidden, "bf16", "f32", seed=hidden + 1, zero_centered_gamma=zc)
+    ref_f = oracle_fwd(case, "rmsnorm", "bf16", "f32", zc)
+    ref = oracle_bwd(case, "rmsnorm", "bf16", "f32", zc, ref_f, add=True)
+    dy, x, r, g = gpu(case, "dy", "x", "residual_dy", "gamma")
+    rs = torch.tensor(ref_f["rsigma"], dtype=torch.float32, device="cuda")
+    out = nf.bwd_add(dy, x, r, rs, g, zero_centered_gamma=zc)
+    checks.check_dx(bits(out["dx"]), ref["dx"], "bf16")
+    checks.check_wgrad(out["dgamma"].cpu().numpy(), ref["dgamma"])
+
+
+def test_bwd_zero_rows_gives_zero_gradients():
+    case = workloads.small_case("layernorm", 4, 256, "bf16", "f32", seed=1)
+    dy, x, g = gpu(case, "dy", "x", "gamma")
+    mu = torch.zeros(0, device="cuda")
+    rs = torch.zeros(0, device="cuda")
+    out = nf.bwd(dy[:0], x[:0], mu, rs, g, norm="layernorm")
+    assert torch.all(out["dgamma"] == 0) and torch.all(out["dbeta"] == 0)
+
+
+def test_fwd_then_bwd_end_to_end():
+    """GPU statistics feeding the GPU backward, against the oracle with its own statistics."""
+    case = workloads.small_case("layernorm", 128, 4096, "bf16", "f32", seed=77)
+    ref_f = oracle_fwd(case, "layernorm", "bf16", "f32", False)
+    ref = oracle_bwd(case, "layernorm", "bf16", "f32", False, ref_f)
+    dy, x, g, b = gpu(case, "dy", "x", "gamma", "beta")
+    f = nf.fwd(x, g, b, norm="layernorm")
+    out = nf.bwd(dy, x, f["mu"], f["rsigma"], g, norm="layernorm")
+    checks.check_dx(bits(out["dx"]), ref["dx"], "bf16")
+    checks.check_wgrad(out["dgamma"].cpu().numpy(), ref["dgamma"])
+
+
+# ------------------------------------------------------------------------------ determinism
+
+def test_repeat_runs_are_bitwise_identical():
+    case = workloads.small_case("layernorm", 500, 20480, "bf16", "f32", seed=8)
+    dy, x, g, b = gpu(case, "dy", "x", "gamma", "beta")
+    outs = []
+    for _ in range(3):
+        f = nf.fwd(x, g, b, norm="layernorm")
+        d = nf.bwd(dy, x[:, :16384].contiguous(), f["mu"], f["rsigma"], g[:16384].contiguous(), norm="layernorm")
+        outs.append((f["y"].clone(), f["mu"].clone(), d["dx"].clone(), d["dgamma"].clone(), d["dbeta"].clone()))
+    for o in outs[1:]:
+        for a, b_ in zip(outs[0], o):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a, b_.view(torch.uint8)
+                               if b_.dtype == torch.bfloat16 else b_)
+    assert_ws_clean()
