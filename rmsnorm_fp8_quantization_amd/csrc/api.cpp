@@ -195,7 +195,8 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   size_t ws = header ? (size_t)kWsHeaderBytes : 0;
   if (pl->band && pl->S > 1) {
     pl->partial_off = ws;
-    ws += round_up((size_t)pl->bands * pl->S * kBandShapes[pl->cfg].rows() * 2 * sizeof(float), 256);
+    const int nv = norm_type == NORM_LAYERNORM ? 2 : 1;
+    ws += round_up((size_t)pl->bands * pl->S * kBandShapes[pl->cfg].rows() * nv * sizeof(uint64_t), 256);
   }
   pl->ws_bytes = ws;
   (void)in_dtype;
@@ -369,7 +370,8 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     rc = occupancy(fn, sh.threads(), &occ);
     if (rc) return rc;
     int64_t grid = cdiv(rows, sh.T);
-    const int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
+    int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
+    if (cap > kMaxGrid) cap = kMaxGrid;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
     rc = launch(fn, dim3((unsigned)grid), dim3(sh.threads()), &f, st);
@@ -381,16 +383,32 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   b.f = f;
   b.y_col = y_colwise;
   b.col_scale_inv = colwise_scale_inv;
-  b.partials = pl.S > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.partial_off) : nullptr;
+  b.partials = pl.S > 1 ? reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + pl.partial_off) : nullptr;
   b.bands = pl.bands;
   b.mx_rows = cdiv(rows, 32);
   b.S = pl.S;
   b.write_row = pl.rowwise ? 1 : 0;
   const void *fn = fwd_band_kernel_ptr(norm_type, in_dtype, pl.mode, pl.colwise, pl.cfg);
   if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no forward band kernel for this combination");
-  int64_t grid = pl.bands * pl.S;
-  if (grid < 1) grid = 1;  // rows == 0 with delayed scaling: one workgroup publishes amax / scale_inv
-  if (grid > 0x7fffffff) return fail(NORM_ERR_UNSUPPORTED, "too many tiles");
+  // persistent grid: at most what fits on the CUs left by the margin; the S workgroups of a
+  // band wait for each other, so at least S must be able to run at once
+  int occ = 1;
+  rc = occupancy(fn, 256, &occ);
+  if (rc) return rc;
+  int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
+  if (cap > kMaxGrid) cap = kMaxGrid;
+  if (pl.S > 1 && cap < 2 * pl.S)
+    return fail(NORM_ERR_UNSUPPORTED, "cu_margin %d leaves too few resident workgroups for %d slices", cu_margin,
+                pl.S);
+  const int64_t tiles = pl.bands * pl.S;
+  int64_t grid = tiles < cap ? tiles : cap;
+  // ticket classes: one per XCD when every class gets several bands and at least 2S workgroups
+  b.classes = 1;
+  if (grid >= (int64_t)kClasses * 2 * pl.S && pl.bands >= (int64_t)kClasses * 4 &&
+      env_int("NORMFP8_BAND_CLASSES", kClasses) == kClasses) {
+    b.classes = kClasses;
+    grid = grid / kClasses * kClasses;
+  }
   rc = launch(fn, dim3((unsigned)grid), dim3(256), &b, st);
   if (rc) return rc;
   return ok();
@@ -497,11 +515,17 @@ int norm_workspace_check(void *stream, void *workspace, uint32_t *flags) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(NORM_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
-  uint32_t words[4] = {0, 0, 0, 0};
+  static uint32_t words[kWsHeaderBytes / 4];
+  static std::mutex mu;
+  std::lock_guard<std::mutex> lk(mu);
   e = hipMemcpy(words, workspace, sizeof(words), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(NORM_ERR_HIP, "hipMemcpy: %s", hipGetErrorString(e));
   uint32_t f = words[kWsError];
-  if (words[kWsDone] != 0 || words[kWsTicket] != 0 || words[kWsAmax] != 0) f |= 2u;
+  // every counter must be back at zero between calls
+  bool dirty = words[kWsDone] != 0;
+  for (int i = 0; i < kClasses; ++i) dirty |= words[kWsTicket0 + i] != 0;
+  for (int i = kWsGroup0; i < kWsAmax0; ++i) dirty |= words[i] != 0;
+  if (dirty) f |= 2u;
   *flags = f;
   if (f) {
     e = hipMemset(static_cast<char *>(workspace) + kWsError * 4, 0, 4);

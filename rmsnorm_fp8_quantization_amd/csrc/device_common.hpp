@@ -70,6 +70,15 @@ template <> __device__ __forceinline__ void strip_to_f32<F16>(const Strip<F16> &
   o[6] = f16_lo(s.v[0].w); o[7] = f16_hi(s.v[0].w);
 }
 
+// Register-pressure barrier: makes the compiler treat a strip's packed registers as changed,
+// so values converted from them before this point are not kept alive to be reused after it
+// (emits no instruction).
+template <class T> __device__ __forceinline__ void opaque(Strip<T> &s) {
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(Strip<T>) / 16); ++i)
+    asm volatile("" : "+v"(s.v[i].x), "+v"(s.v[i].y), "+v"(s.v[i].z), "+v"(s.v[i].w));
+}
+
 template <class T>
 __device__ __forceinline__ void load_strip(Strip<T> &s, const void *base, int64_t elem) {
   const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + elem * T::bytes);
@@ -306,19 +315,93 @@ __device__ __forceinline__ void vmem_drain() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
 }
 
-// Spin until *p >= target. Gives up after `limit` ticks of the 100 MHz real-time counter and
-// records the time-out in the header's error word (the caller then proceeds with whatever
-// partner data is present, so a corrupt header cannot hang the GPU).
-__device__ __forceinline__ void spin_until_ge(const uint32_t *p, uint32_t target, uint32_t *err) {
-  if (ld_dev_u32(p) >= target) return;
+__device__ __forceinline__ void st_dev64(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t *p) {
+  return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
+  return ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
+}
+// the tag of the launch that observed `epoch` at its start (never 0)
+__device__ __forceinline__ uint32_t epoch_tag(uint32_t epoch) { return epoch == 0xffffffffu ? 1u : epoch + 1u; }
+
+// Value of a tagged word once it carries `tag` (polls; time-limited like spin_until_ge).
+__device__ __forceinline__ float wait_tagged(const uint64_t *p, uint32_t tag, uint32_t *err) {
+  uint64_t v = ld_dev64(p);
+  if ((uint32_t)(v >> 32) == tag) return __uint_as_float((uint32_t)v);
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (ld_dev_u32(p) < target) {
-    __builtin_amdgcn_s_sleep(2);
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    v = ld_dev64(p);
+    if ((uint32_t)(v >> 32) == tag) break;
     if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
       or_dev(err, 1u);
-      return;
+      break;
     }
   }
+  return __uint_as_float((uint32_t)v);
+}
+
+
+// ------------------------------------------------------------------------------------------
+// launch completion without a hot spot: workgroup g counts itself in group g / 64; the
+// workgroup completing a group counts the group in kWsDone. Exactly one workgroup -- the last
+// to finish -- sees both counters complete. Call from every thread after all of the
+// workgroup's cross-workgroup results are stored (after vmem_drain); returns the same answer
+// in every thread of the workgroup.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ bool finish_workgroup(uint32_t *ws, uint32_t *lds_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int g = blockIdx.x / kWsGroupSize;
+    const int ngroups = ((int)gridDim.x + kWsGroupSize - 1) / kWsGroupSize;
+    const int rem = (int)gridDim.x - g * kWsGroupSize;
+    const int gsize = rem < kWsGroupSize ? rem : kWsGroupSize;
+    bool last = false;
+    if (add_dev(ws + kWsGroup0 + g, 1u) == (uint32_t)(gsize - 1))
+      last = add_dev(ws + kWsDone, 1u) == (uint32_t)(ngroups - 1);
+    *lds_flag = last ? 1u : 0u;
+  }
+  __syncthreads();
+  return *lds_flag != 0u;
+}
+
+// this workgroup's amax entry, tagged with its launch
+__device__ __forceinline__ void publish_amax(uint32_t *ws, float a, uint32_t tag) {
+  st_dev64(reinterpret_cast<uint64_t *>(ws + kWsAmax0) + blockIdx.x, tagged(a, tag));
+}
+
+// max over the per-workgroup amax entries [0, n) (all threads of the last workgroup)
+__device__ __forceinline__ float gather_amax(uint32_t *ws, int n, float *lds_red, uint32_t tag) {
+  const uint64_t *parts = reinterpret_cast<const uint64_t *>(ws + kWsAmax0);
+  float a = 0.0f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) a = fmaxf(a, wait_tagged(parts + i, tag, ws + kWsError));
+  a = wave_max(a);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds_red[w] = a;
+  __syncthreads();
+  float t = 0.0f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t = fmaxf(t, lds_red[i]);
+  return t;
+}
+
+// re-zero the completion counters and advance the epoch (all threads of the last workgroup)
+__device__ __forceinline__ void reset_completion(uint32_t *ws) {
+  const int ngroups = ((int)gridDim.x + kWsGroupSize - 1) / kWsGroupSize;
+  for (int i = threadIdx.x; i < ngroups; i += blockDim.x) xchg_dev(ws + kWsGroup0 + i, 0u);
+  if (threadIdx.x == 0) {
+    xchg_dev(ws + kWsDone, 0u);
+    add_dev(ws + kWsEpoch, 1u);
+  }
+}
+
+// epoch of the current launch (read by thread 0 at the start; broadcast through LDS)
+__device__ __forceinline__ uint32_t read_epoch(uint32_t *ws, uint32_t *lds) {
+  if (threadIdx.x == 0) *lds = ld_dev_u32(ws + kWsEpoch);
+  __syncthreads();
+  return *lds;
 }
 
 }  // namespace nf8

@@ -15,9 +15,12 @@
 // S - 1 workgroups of its band; every workgroup then merges the S partials in slice order, so
 // all S hold bit-identical statistics.
 //
-// Tiles are handed out in ticket order (an atomic counter taken when the workgroup starts), so
-// the workgroups of a band are always co-resident: at any time only the newest band can be
-// waiting for a member that has not started yet, and every older band's members are running.
+// Tiles are handed out in ticket order from an atomic counter, and a workgroup takes its next
+// ticket only after it has stopped waiting on its current band. So a workgroup never holds a
+// ticket of a band it is waiting on, every ticket holder is running, and at any time only the
+// newest band can be waiting for a member whose ticket has not been taken yet: with at least
+// 2S workgroups per ticket class some workgroup is always free to take it. No assumption about
+// how many workgroups are resident is needed.
 //
 // Columnwise outputs: y_col is [hidden, rows]. MXFP8 columnwise blocks are the 32 rows of one
 // band (RW = 8): each lane takes the max over its 8 rows per column, the 4 waves combine
@@ -91,317 +94,338 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
   const int64_t N = p.rows;
   const int fmt = p.out_dtype;
 
-  __shared__ int64_t s_ticket;
+  constexpr int NV = NORM == NT_LAYERNORM ? 2 : 1;  // tagged words per row partial
+  __shared__ int64_t s_next;
   __shared__ uint32_t s_last;
+  __shared__ uint32_t s_epoch;
+  __shared__ float wred[4];
   __shared__ float colmax[MXCOL ? 4 : 1][MXCOL ? CW : 1];
-  __shared__ float xpart[4][RW][kMaxSlices][2];  // fetched partials of the band's rows
+  __shared__ float xpart[4][RW][kMaxSlices][NV];  // fetched partials of the band's rows
 
-  int64_t band;
-  int slice;
+  // Ticket class: the workgroups with the same blockIdx % classes serve one contiguous range
+  // of bands. Consecutive workgroups are dispatched to the XCDs in turn, so a class's bands --
+  // and the columnwise segments that neighbouring bands write into the same cache lines --
+  // stay within one L2.
+  const int ncls = bp.classes;
+  const int cls = (int)(blockIdx.x % ncls);
+  const int64_t wpc = gridDim.x / ncls;
+  const int64_t lwg = blockIdx.x / ncls;
+  const int64_t b0 = bp.bands * cls / ncls;
+  const int64_t b1 = bp.bands * (cls + 1) / ncls;
+  const int64_t ntiles = (b1 - b0) * S;
+  uint32_t *const ticket = S > 1 ? p.ws + kWsTicket0 + cls : nullptr;
+  const bool coordinated = MODE == MODE_DELAYED || S > 1;
+  const uint32_t tag = coordinated ? epoch_tag(read_epoch(p.ws, &s_epoch)) : 0u;
+
+  int64_t tk;
   if (S == 1) {
-    band = blockIdx.x;
-    slice = 0;
+    tk = lwg;
   } else {
-    if (tid == 0) s_ticket = (int64_t)add_dev(p.ws + kWsTicket, 1u);
+    if (tid == 0) s_next = (int64_t)add_dev(ticket, 1u);
     __syncthreads();
-    const int64_t t = s_ticket;
-    band = t / S;
-    slice = (int)(t - band * S);
-  }
-  const int64_t rbase = band * R + wave * RW;  // first row of this wave
-  const int64_t cbase = (int64_t)slice * CW;
-
-  // Weights are read per strip where they are used (they stay in L1/L2 for the tile's rows)
-  // instead of being held in registers for every strip of the tile.
-  bool cv[KC];
-#pragma unroll
-  for (int k = 0; k < KC; ++k) cv[k] = cbase + 8 * (lane + 64 * k) < H;
-  auto weights = [&](int k, float (&g)[8], float (&bt)[8]) {
-    const int64_t col = cbase + 8 * (lane + 64 * k);
-    if (cv[k]) {
-      load_w8(g, p.gamma, col, p.w_dtype);
-      if (p.zero_centered) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) g[i] += 1.0f;
-      }
-      if constexpr (NORM == NT_LAYERNORM) load_w8(bt, p.beta, col, p.w_dtype);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        g[i] = 0.0f;
-        bt[i] = 0.0f;
-      }
-    }
-  };
-
-  Strip<IN> xs[RW][KC];
-#pragma unroll
-  for (int j = 0; j < RW; ++j)
-#pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      const int64_t row = rbase + j;
-      if (row < N && cv[k]) load_strip<IN>(xs[j][k], p.x, row * H + cbase + 8 * (lane + 64 * k));
-      else zero_strip<IN>(xs[j][k]);
-    }
-
-  // ---- per-row partial statistics of this slice (wave-merged)
-  Stats st[RW];
-#pragma unroll
-  for (int j = 0; j < RW; ++j) {
-    const bool rv = rbase + j < N;
-    if constexpr (NORM == NT_LAYERNORM) {
-      float s = 0.0f, n = 0.0f;
-#pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        float xv[8];
-        strip_to_f32<IN>(xs[j][k], xv);
-        if (rv && cv[k]) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) s += xv[i];
-          n += 8.0f;
-        }
-      }
-      const float m = n > 0.0f ? s / n : 0.0f;
-      float q = 0.0f;
-#pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        float xv[8];
-        strip_to_f32<IN>(xs[j][k], xv);
-        if (rv && cv[k]) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float d = xv[i] - m;
-            q = fmaf(d, d, q);
-          }
-        }
-      }
-      st[j] = wave_merge(Stats{n, m, q});
-    } else {
-      float q = 0.0f;
-#pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        float xv[8];
-        strip_to_f32<IN>(xs[j][k], xv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q = fmaf(xv[i], xv[i], q);
-      }
-      st[j] = Stats{0.0f, 0.0f, wave_sum(q)};
-    }
-  }
-
-  // ---- combine the S slices of the band through the workspace
-  if (S > 1) {
-    float *part = bp.partials + (band * S + slice) * (int64_t)R * 2;
-#pragma unroll
-    for (int j = 0; j < RW; ++j) {
-      if (lane == j) {
-        st_dev(part + 2 * (wave * RW + j), st[j].mean);
-        st_dev(part + 2 * (wave * RW + j) + 1, st[j].m2);
-      }
-    }
-    vmem_drain();
+    tk = s_next;
     __syncthreads();
-    if (tid == 0) {
-      uint32_t *slot = p.ws + kWsSlot0 + (band % kWsSlots);
-      const uint32_t q = (uint32_t)(band / kWsSlots);
-      uint32_t *err = p.ws + kWsError;
-      spin_until_ge(slot, q * (uint32_t)S, err);  // previous band on this slot has arrived
-      add_dev(slot, 1u);
-      spin_until_ge(slot, (q + 1) * (uint32_t)S, err);  // all S slices of this band arrived
-    }
-    __syncthreads();
-    // every lane fetches one (row, slice) partial at once; lane j then merges row j's S
-    // partials in slice order from LDS and broadcasts the result to the wave
-    const float *bpart = bp.partials + band * S * (int64_t)R * 2;
-    for (int l = lane; l < RW * S; l += 64) {
-      const int j = l / S, s = l - (l / S) * S;
-      const float *e = bpart + ((int64_t)s * R + wave * RW + j) * 2;
-      xpart[wave][j][s][0] = ld_dev(e);
-      xpart[wave][j][s][1] = ld_dev(e + 1);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < RW; ++j) {
-      Stats acc{0.0f, 0.0f, 0.0f};
-      if (lane == j) {
-        for (int s = 0; s < S; ++s) {
-          const float mean = xpart[wave][j][s][0], m2 = xpart[wave][j][s][1];
-          if constexpr (NORM == NT_LAYERNORM) {
-            const int64_t left = H - (int64_t)s * CW;
-            const float n = (float)(left < CW ? left : CW);
-            acc = chan_merge(acc, Stats{n, mean, m2});
-          } else {
-            acc.m2 += m2;
-          }
-        }
-      }
-      st[j].mean = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc.mean), j));
-      st[j].m2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc.m2), j));
-    }
-  }
-
-  const float inv_h = 1.0f / (float)H;
-  float mu[RW], rs[RW];
-#pragma unroll
-  for (int j = 0; j < RW; ++j) {
-    mu[j] = NORM == NT_LAYERNORM ? st[j].mean : 0.0f;
-    rs[j] = 1.0f / sqrtf(st[j].m2 * inv_h + p.eps);
-    const int64_t row = rbase + j;
-    if (slice == 0 && lane == j && row < N) {
-      if (p.rsigma) p.rsigma[row] = rs[j];
-      if constexpr (NORM == NT_LAYERNORM) {
-        if (p.mu) p.mu[row] = mu[j];
-      }
-    }
   }
 
   float scale = 1.0f;
   if constexpr (MODE == MODE_DELAYED) scale = *p.scale;
   float amax_local = 0.0f;
-  const int valid_rows = (int)(N - rbase < RW ? (N - rbase < 0 ? 0 : N - rbase) : RW);
+  const float inv_h = 1.0f / (float)H;
   const bool col_aligned = (N % RW) == 0;
 
-  // ---- MXFP8 columnwise block maxima (32 rows = the 4 waves' rows of this band)
-  if constexpr (MXCOL) {
-#pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      float cm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      float gk[8], bk[8];
-      weights(k, gk, bk);
-#pragma unroll
-      for (int j = 0; j < RW; ++j) {
-        float xv[8];
-        strip_to_f32<IN>(xs[j][k], xv);
-        if (j < valid_rows) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            float y;
-            if constexpr (NORM == NT_LAYERNORM) y = fmaf((xv[i] - mu[j]) * rs[j], gk[i], bk[i]);
-            else y = (xv[i] * rs[j]) * gk[i];
-            cm[i] = fmaxf(cm[i], fabsf(y));
-          }
-        }
-      }
-      float4 *dst = reinterpret_cast<float4 *>(&colmax[wave][8 * (lane + 64 * k)]);
-      dst[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
-      dst[1] = make_float4(cm[4], cm[5], cm[6], cm[7]);
-    }
-    __syncthreads();
-  }
+  while (tk < ntiles) {
+    const int64_t lband = tk / S;
+    const int64_t band = b0 + lband;
+    const int slice = (int)(tk - lband * S);
+    const int64_t rbase = band * R + wave * RW;  // first row of this wave
+    const int64_t cbase = (int64_t)slice * CW;
 
-  // ---- outputs, one strip column at a time
+    // Weights are read per strip where they are used (they stay in L1/L2 for the tile's rows)
+    // instead of being held in registers for every strip of the tile.
+    bool cv[KC];
 #pragma unroll
-  for (int k = 0; k < KC; ++k) {
-    const int64_t col = cbase + 8 * (lane + 64 * k);
-    float gk[8], bk[8];
-    weights(k, gk, bk);
-    uint2 rcodes[RW];  // rowwise codes (delayed: reused for the columnwise transpose)
-    float colf[8];     // MX columnwise: 2^-X per column
-    int colx[8];
-    if constexpr (MXCOL) {
+    for (int k = 0; k < KC; ++k) cv[k] = cbase + 8 * (lane + 64 * k) < H;
+    auto weights = [&](int k, float (&g)[8], float (&bt)[8]) {
+      const int64_t col = cbase + 8 * (lane + 64 * k);
+      if (cv[k]) {
+        load_w8(g, p.gamma, col, p.w_dtype);
+        if (p.zero_centered) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = 8 * (lane + 64 * k) + i;
-        const float a = fmaxf(fmaxf(colmax[0][c], colmax[1][c]), fmaxf(colmax[2][c], colmax[3][c]));
-        colx[i] = mx_exponent(a, fmt);
-        colf[i] = exp2_neg(colx[i]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < RW; ++j) {
-      const int64_t row = rbase + j;
-      const bool ok = (j < valid_rows) && cv[k];
-      float xv[8], y[8];
-      strip_to_f32<IN>(xs[j][k], xv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (NORM == NT_LAYERNORM) y[i] = fmaf((xv[i] - mu[j]) * rs[j], gk[i], bk[i]);
-        else y[i] = (xv[i] * rs[j]) * gk[i];
-      }
-      if constexpr (MODE == MODE_PLAIN) {
-        if (ok) store_out8(p.y, row * H + col, y, p.out_dtype);
-      } else if constexpr (MODE == MODE_DELAYED) {
-        float u[8];
+          for (int i = 0; i < 8; ++i) g[i] += 1.0f;
+        }
+        if constexpr (NORM == NT_LAYERNORM) load_w8(bt, p.beta, col, p.w_dtype);
+      } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          u[i] = y[i] * scale;
-          if (ok) amax_local = fmaxf(amax_local, fabsf(y[i]));
+          g[i] = 0.0f;
+          bt[i] = 0.0f;
         }
-        rcodes[j] = fp8_pack8(u, fmt);
-        if (ok && bp.write_row) *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.y) + row * H + col) = rcodes[j];
-      } else {  // MX
-        if (bp.write_row) {
-          float a = 0.0f;
+      }
+    };
+
+    Strip<IN> xs[RW][KC];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[i]));
-          a = quad_max(ok ? a : 0.0f);
-          const int X = mx_exponent(a, fmt);
-          const float f = exp2_neg(X);
-          float u[8];
+    for (int j = 0; j < RW; ++j)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) u[i] = y[i] * f;
-          const uint2 c = fp8_pack8(u, fmt);
-          if (ok) {
-            *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.y) + row * H + col) = c;
-            if ((lane & 3) == 0)
-              static_cast<uint8_t *>(p.scale_inv)[row * p.mx_cols + (col >> 5)] = (uint8_t)(X + 127);
+      for (int k = 0; k < KC; ++k) {
+        const int64_t row = rbase + j;
+        if (row < N && cv[k]) load_strip<IN>(xs[j][k], p.x, row * H + cbase + 8 * (lane + 64 * k));
+        else zero_strip<IN>(xs[j][k]);
+      }
+
+    // ---- per-row partial statistics of this slice (wave-merged)
+    Stats st[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      const bool rv = rbase + j < N;
+      if constexpr (NORM == NT_LAYERNORM) {
+        float sm = 0.0f, n = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          float xv[8];
+          strip_to_f32<IN>(xs[j][k], xv);
+          if (rv && cv[k]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sm += xv[i];
+            n += 8.0f;
           }
         }
-        if constexpr (MXCOL) {
+        const float m = n > 0.0f ? sm / n : 0.0f;
+        float q = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          float xv[8];
+          strip_to_f32<IN>(xs[j][k], xv);
+          if (rv && cv[k]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float d = xv[i] - m;
+              q = fmaf(d, d, q);
+            }
+          }
+        }
+        st[j] = wave_merge(Stats{n, m, q});
+      } else {
+        float q = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          float xv[8];
+          strip_to_f32<IN>(xs[j][k], xv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) q = fmaf(xv[i], xv[i], q);
+        }
+        st[j] = Stats{0.0f, 0.0f, wave_sum(q)};
+      }
+    }
+
+    // ---- combine the S slices of the band through the workspace: publish this slice's
+    // tagged row partials, then every lane polls one (row, slice, word) of the band until it
+    // carries this launch's tag; lane j merges row j's S partials in slice order from LDS and
+    // broadcasts the result to the wave
+    if (S > 1) {
+      uint64_t *part = bp.partials + (band * S + slice) * (int64_t)R * NV;
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        if (lane == j) {
+          if constexpr (NORM == NT_LAYERNORM) {
+            st_dev64(part + (wave * RW + j) * NV, tagged(st[j].mean, tag));
+            st_dev64(part + (wave * RW + j) * NV + 1, tagged(st[j].m2, tag));
+          } else {
+            st_dev64(part + (wave * RW + j), tagged(st[j].m2, tag));
+          }
+        }
+      }
+      const uint64_t *bpart = bp.partials + band * S * (int64_t)R * NV;
+      for (int l = lane; l < RW * S * NV; l += 64) {
+        const int v = l % NV, js = l / NV;
+        const int j = js / S, sl = js - (js / S) * S;
+        xpart[wave][j][sl][v] = wait_tagged(bpart + ((int64_t)sl * R + wave * RW + j) * NV + v, tag, p.ws + kWsError);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        Stats acc{0.0f, 0.0f, 0.0f};
+        if (lane == j) {
+          for (int sl = 0; sl < S; ++sl) {
+            if constexpr (NORM == NT_LAYERNORM) {
+              const int64_t left = H - (int64_t)sl * CW;
+              const float n = (float)(left < CW ? left : CW);
+              acc = chan_merge(acc, Stats{n, xpart[wave][j][sl][0], xpart[wave][j][sl][1]});
+            } else {
+              acc.m2 += xpart[wave][j][sl][0];
+            }
+          }
+        }
+        st[j].mean = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc.mean), j));
+        st[j].m2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc.m2), j));
+      }
+    }
+    // The next tile's ticket is taken only now, once this workgroup waits for nothing more in
+    // its current band (a ticket taken earlier could be a slice of the band it is waiting on,
+    // which it could then never deliver); its latency overlaps the output phase.
+    if (S > 1 && tid == 0) s_next = (int64_t)add_dev(ticket, 1u);
+
+    float mu[RW], rs[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      mu[j] = NORM == NT_LAYERNORM ? st[j].mean : 0.0f;
+      rs[j] = 1.0f / sqrtf(st[j].m2 * inv_h + p.eps);
+      const int64_t row = rbase + j;
+      if (slice == 0 && lane == j && row < N) {
+        if (p.rsigma) p.rsigma[row] = rs[j];
+        if constexpr (NORM == NT_LAYERNORM) {
+          if (p.mu) p.mu[row] = mu[j];
+        }
+      }
+    }
+    const int valid_rows = (int)(N - rbase < RW ? (N - rbase < 0 ? 0 : N - rbase) : RW);
+
+    // ---- MXFP8 columnwise block maxima (32 rows = the 4 waves' rows of this band)
+#pragma unroll
+    for (int j = 0; j < RW; ++j)
+#pragma unroll
+      for (int k = 0; k < KC; ++k) opaque<IN>(xs[j][k]);
+    if constexpr (MXCOL) {
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float cm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        float gk[8], bk[8];
+        weights(k, gk, bk);
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+          float xv[8];
+          strip_to_f32<IN>(xs[j][k], xv);
+          if (j < valid_rows) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              float y;
+              if constexpr (NORM == NT_LAYERNORM) y = fmaf((xv[i] - mu[j]) * rs[j], gk[i], bk[i]);
+              else y = (xv[i] * rs[j]) * gk[i];
+              cm[i] = fmaxf(cm[i], fabsf(y));
+            }
+          }
+        }
+        float4 *dst = reinterpret_cast<float4 *>(&colmax[wave][8 * (lane + 64 * k)]);
+        dst[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+        dst[1] = make_float4(cm[4], cm[5], cm[6], cm[7]);
+      }
+      __syncthreads();
+    }
+
+    // ---- outputs, one strip column at a time
+#pragma unroll
+    for (int j = 0; j < RW; ++j)
+#pragma unroll
+      for (int k = 0; k < KC; ++k) opaque<IN>(xs[j][k]);
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int64_t col = cbase + 8 * (lane + 64 * k);
+      float gk[8], bk[8];
+      weights(k, gk, bk);
+      uint2 rcodes[RW];  // rowwise codes (delayed: reused for the columnwise transpose)
+      float colf[8];     // MX columnwise: 2^-X per column
+      int colx[8];
+      if constexpr (MXCOL) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = 8 * (lane + 64 * k) + i;
+          const float a = fmaxf(fmaxf(colmax[0][c], colmax[1][c]), fmaxf(colmax[2][c], colmax[3][c]));
+          colx[i] = mx_exponent(a, fmt);
+          colf[i] = exp2_neg(colx[i]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const int64_t row = rbase + j;
+        const bool ok = (j < valid_rows) && cv[k];
+        float xv[8], y[8];
+        strip_to_f32<IN>(xs[j][k], xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if constexpr (NORM == NT_LAYERNORM) y[i] = fmaf((xv[i] - mu[j]) * rs[j], gk[i], bk[i]);
+          else y[i] = (xv[i] * rs[j]) * gk[i];
+        }
+        if constexpr (MODE == MODE_PLAIN) {
+          if (ok) store_out8(p.y, row * H + col, y, p.out_dtype);
+        } else if constexpr (MODE == MODE_DELAYED) {
           float u[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) u[i] = y[i] * colf[i];
+          for (int i = 0; i < 8; ++i) {
+            u[i] = y[i] * scale;
+            if (ok) amax_local = fmaxf(amax_local, fabsf(y[i]));
+          }
           rcodes[j] = fp8_pack8(u, fmt);
+          if (ok && bp.write_row)
+            *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.y) + row * H + col) = rcodes[j];
+        } else {  // MX
+          if (bp.write_row) {
+            float a = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[i]));
+            a = quad_max(ok ? a : 0.0f);
+            const int X = mx_exponent(a, fmt);
+            const float f = exp2_neg(X);
+            float u[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] = y[i] * f;
+            const uint2 c = fp8_pack8(u, fmt);
+            if (ok) {
+              *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.y) + row * H + col) = c;
+              if ((lane & 3) == 0)
+                static_cast<uint8_t *>(p.scale_inv)[row * p.mx_cols + (col >> 5)] = (uint8_t)(X + 127);
+            }
+          }
+          if constexpr (MXCOL) {
+            float u[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] = y[i] * colf[i];
+            rcodes[j] = fp8_pack8(u, fmt);
+          }
         }
       }
-    }
-    if constexpr (COL && MODE != MODE_PLAIN) {
-      if (cv[k] && valid_rows > 0) {
-        uint8_t *colp = static_cast<uint8_t *>(bp.y_col) + col * N + rbase;
-        store_col_codes<RW>(rcodes, colp, N, valid_rows, col_aligned);
-        if constexpr (MXCOL) {
-          if (wave == 0) {
+      if constexpr (COL && MODE != MODE_PLAIN) {
+        if (cv[k] && valid_rows > 0) {
+          uint8_t *colp = static_cast<uint8_t *>(bp.y_col) + col * N + rbase;
+          store_col_codes<RW>(rcodes, colp, N, valid_rows, col_aligned);
+          if constexpr (MXCOL) {
+            if (wave == 0) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-              static_cast<uint8_t *>(bp.col_scale_inv)[(col + i) * bp.mx_rows + band] = (uint8_t)(colx[i] + 127);
+              for (int i = 0; i < 8; ++i)
+                static_cast<uint8_t *>(bp.col_scale_inv)[(col + i) * bp.mx_rows + band] = (uint8_t)(colx[i] + 127);
+            }
           }
         }
       }
     }
+    __syncthreads();  // LDS (colmax, xpart) is reused by the next tile; s_next is visible
+    tk = S > 1 ? s_next : tk + wpc;
   }
 
-  // ---- end of launch: amax publication and header reset by the last workgroup
-  const bool need_done = (MODE == MODE_DELAYED) || (S > 1);
-  if (need_done) {
-    if constexpr (MODE == MODE_DELAYED) {
-      const float m = wave_max(amax_local);
-      if (lane == 0) max_dev(p.ws + kWsAmax, __float_as_uint(m));
-    }
-    vmem_drain();
+  // ---- end of launch: amax publication and counter reset by the last workgroup
+  if constexpr (MODE == MODE_DELAYED) {
+    const float m = wave_max(amax_local);
+    if (lane == 0) wred[wave] = m;
     __syncthreads();
-    if (tid == 0) s_last = add_dev(p.ws + kWsDone, 1u) == gridDim.x - 1 ? 1u : 0u;
-    __syncthreads();
-    if (s_last) {
-      if constexpr (MODE == MODE_DELAYED) {
-        if (tid == 0) {
-          const float tot = __uint_as_float(xchg_dev(p.ws + kWsAmax, 0u));
-          *p.updated_amax = fmaxf(*p.amax_in, tot);
-        }
+    if (tid == 0) {
+      publish_amax(p.ws, fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3])), tag);
+      if (blockIdx.x == 0) {
+        if (p.scale_inv) *static_cast<float *>(p.scale_inv) = 1.0f / scale;
+        if (bp.col_scale_inv) *static_cast<float *>(bp.col_scale_inv) = 1.0f / scale;
       }
-      if (S > 1) {
-        const int64_t used = bp.bands < kWsSlots ? bp.bands : kWsSlots;
-        for (int64_t i = tid; i < used; i += 256) xchg_dev(p.ws + kWsSlot0 + i, 0u);
-        if (tid == 0) xchg_dev(p.ws + kWsTicket, 0u);
-      }
-      vmem_drain();
-      __syncthreads();
-      if (tid == 0) xchg_dev(p.ws + kWsDone, 0u);
     }
   }
-  if constexpr (MODE == MODE_DELAYED) {
-    if (band == 0 && slice == 0 && tid == 0) {
-      if (p.scale_inv) *static_cast<float *>(p.scale_inv) = 1.0f / scale;
-      if (bp.col_scale_inv) *static_cast<float *>(bp.col_scale_inv) = 1.0f / scale;
+  if (coordinated) {
+    vmem_drain();
+    if (finish_workgroup(p.ws, &s_last)) {
+      if constexpr (MODE == MODE_DELAYED) {
+        __syncthreads();
+        const float tot = gather_amax(p.ws, gridDim.x, wred, tag);
+        if (tid == 0) *p.updated_amax = fmaxf(*p.amax_in, tot);
+      }
+      if (S > 1 && tid < ncls) xchg_dev(p.ws + kWsTicket0 + tid, 0u);
+      vmem_drain();
+      __syncthreads();
+      reset_completion(p.ws);
     }
   }
 }

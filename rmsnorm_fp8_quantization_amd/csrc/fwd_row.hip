@@ -22,9 +22,16 @@
 
 namespace nf8 {
 
-template <int NORM, class IN, int MODE, int P, int T, int KC>
+// WL: where the weights live while the workgroup walks its rows. 0: each lane keeps its
+// columns' gamma / beta in registers; 1: the workgroup stages them once in LDS (as float32,
+// 1 + gamma when zero-centred), leaving the registers to the row data so that the next row
+// can be in flight while the current one is normalised.
+template <int NORM, class IN, int MODE, int P, int T, int KC, int WL>
 __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   constexpr int TEAM = 64 * P;
+  constexpr int NT = TEAM * T;
+  constexpr int COVER = 8 * TEAM * KC;                      // row elements one team holds
+  constexpr int NW = NORM == NT_LAYERNORM ? 2 : 1;          // weight arrays
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -34,67 +41,126 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   const int64_t H = p.hidden;
   const int fmt = p.out_dtype;
 
-  // columns of this lane, effective weight (1 + gamma when zero-centred) and beta
   bool cv[KC];
-  float g[KC][8];
-  float b[NORM == NT_LAYERNORM ? KC : 1][8];
 #pragma unroll
-  for (int k = 0; k < KC; ++k) {
-    const int64_t col = 8 * (int64_t)(tl + TEAM * k);
-    cv[k] = col < H;
-    if (cv[k]) {
-      load_w8(g[k], p.gamma, col, p.w_dtype);
+  for (int k = 0; k < KC; ++k) cv[k] = 8 * (int64_t)(tl + TEAM * k) < H;
+
+  // ---- weights
+  __shared__ float wlds[WL ? NW * COVER : 1];
+  float g[WL ? 1 : KC][8];
+  float b[(!WL && NORM == NT_LAYERNORM) ? KC : 1][8];
+  if constexpr (WL) {
+    for (int64_t c = 8 * (int64_t)tid; c < H; c += 8 * NT) {
+      float w[8];
+      load_w8(w, p.gamma, c, p.w_dtype);
       if (p.zero_centered) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) g[k][i] += 1.0f;
+        for (int i = 0; i < 8; ++i) w[i] += 1.0f;
       }
-      if constexpr (NORM == NT_LAYERNORM) load_w8(b[k], p.beta, col, p.w_dtype);
-    } else {
+      float4 *d = reinterpret_cast<float4 *>(wlds + c);
+      d[0] = make_float4(w[0], w[1], w[2], w[3]);
+      d[1] = make_float4(w[4], w[5], w[6], w[7]);
+      if constexpr (NORM == NT_LAYERNORM) {
+        load_w8(w, p.beta, c, p.w_dtype);
+        float4 *e = reinterpret_cast<float4 *>(wlds + COVER + c);
+        e[0] = make_float4(w[0], w[1], w[2], w[3]);
+        e[1] = make_float4(w[4], w[5], w[6], w[7]);
+      }
+    }
+    __syncthreads();
+  } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        g[k][i] = 0.0f;
-        if constexpr (NORM == NT_LAYERNORM) b[k][i] = 0.0f;
+    for (int k = 0; k < KC; ++k) {
+      const int64_t col = 8 * (int64_t)(tl + TEAM * k);
+      if (cv[k]) {
+        load_w8(g[k], p.gamma, col, p.w_dtype);
+        if (p.zero_centered) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) g[k][i] += 1.0f;
+        }
+        if constexpr (NORM == NT_LAYERNORM) load_w8(b[k], p.beta, col, p.w_dtype);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          g[k][i] = 0.0f;
+          if constexpr (NORM == NT_LAYERNORM) b[k][i] = 0.0f;
+        }
       }
     }
   }
+  // the 8 weights of strip k (from LDS or registers)
+  auto weights = [&](int k, float (&gk)[8], float (&bk)[8]) {
+    if constexpr (WL) {
+      const int c = 8 * (tl + TEAM * k);
+      const float4 *s0 = reinterpret_cast<const float4 *>(wlds + c);
+      float4 a = s0[0], d = s0[1];
+      gk[0] = a.x; gk[1] = a.y; gk[2] = a.z; gk[3] = a.w; gk[4] = d.x; gk[5] = d.y; gk[6] = d.z; gk[7] = d.w;
+      if constexpr (NORM == NT_LAYERNORM) {
+        const float4 *s1 = reinterpret_cast<const float4 *>(wlds + COVER + c);
+        a = s1[0];
+        d = s1[1];
+        bk[0] = a.x; bk[1] = a.y; bk[2] = a.z; bk[3] = a.w; bk[4] = d.x; bk[5] = d.y; bk[6] = d.z; bk[7] = d.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        gk[i] = g[k][i];
+        if constexpr (NORM == NT_LAYERNORM) bk[i] = b[k][i];
+      }
+    }
+  };
+
   float scale = 1.0f;
-  if constexpr (MODE == MODE_DELAYED) scale = *p.scale;
+  uint32_t tag = 0;
+  __shared__ uint32_t s_epoch;
+  if constexpr (MODE == MODE_DELAYED) {
+    scale = *p.scale;
+    tag = epoch_tag(read_epoch(p.ws, &s_epoch));
+  }
   float amax_local = 0.0f;
 
   __shared__ Stats red[2][T][P];
   const float inv_h = 1.0f / (float)H;
+  const int64_t stride = (int64_t)gridDim.x * T;
 
-  int iter = 0;
-  for (int64_t base = (int64_t)blockIdx.x * T; base < p.rows; base += (int64_t)gridDim.x * T, ++iter) {
-    const int64_t row = base + team;
-    const bool rv = row < p.rows;
-    Strip<IN> xs[KC];
+  auto load_row = [&](Strip<IN> (&xs)[KC], int64_t row) {
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      if (rv && cv[k]) load_strip<IN>(xs[k], p.x, row * H + 8 * (int64_t)(tl + TEAM * k));
+      if (row < p.rows && cv[k]) load_strip<IN>(xs[k], p.x, row * H + 8 * (int64_t)(tl + TEAM * k));
       else zero_strip<IN>(xs[k]);
     }
+  };
+
+  // software pipeline: the next row's loads are issued before the current row is normalised
+  Strip<IN> cur[KC], nxt[KC];
+  int64_t base = (int64_t)blockIdx.x * T;
+  load_row(cur, base + team);
+  int iter = 0;
+  for (; base < p.rows; base += stride, ++iter) {
+    const int64_t row = base + team;
+    const bool rv = row < p.rows;
+    load_row(nxt, base + stride + team);
 
     // ---- lane-local statistics over its valid strips
     Stats st{0.0f, 0.0f, 0.0f};
     if constexpr (NORM == NT_LAYERNORM) {
-      float s = 0.0f, n = 0.0f;
+      float sm = 0.0f, n = 0.0f;
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
         float xv[8];
-        strip_to_f32<IN>(xs[k], xv);
+        strip_to_f32<IN>(cur[k], xv);
         if (rv && cv[k]) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) s += xv[i];
+          for (int i = 0; i < 8; ++i) sm += xv[i];
           n += 8.0f;
         }
       }
-      const float m = n > 0.0f ? s / n : 0.0f;
+      const float m = n > 0.0f ? sm / n : 0.0f;
       float q = 0.0f;
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
         float xv[8];
-        strip_to_f32<IN>(xs[k], xv);
+        strip_to_f32<IN>(cur[k], xv);
         if (rv && cv[k]) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -103,14 +169,13 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
           }
         }
       }
-      st = Stats{n, m, q};
-      st = wave_merge(st);
+      st = wave_merge(Stats{n, m, q});
     } else {
       float q = 0.0f;
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
         float xv[8];
-        strip_to_f32<IN>(xs[k], xv);
+        strip_to_f32<IN>(cur[k], xv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) q = fmaf(xv[i], xv[i], q);  // masked strips are zero
       }
@@ -130,13 +195,8 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
       }
     }
 
-    float mu = 0.0f, rs;
-    if constexpr (NORM == NT_LAYERNORM) {
-      mu = st.mean;
-      rs = 1.0f / sqrtf(st.m2 * inv_h + p.eps);
-    } else {
-      rs = 1.0f / sqrtf(st.m2 * inv_h + p.eps);
-    }
+    const float mu = NORM == NT_LAYERNORM ? st.mean : 0.0f;
+    const float rs = 1.0f / sqrtf(st.m2 * inv_h + p.eps);
     if (rv && tl == 0) {
       if (p.rsigma) p.rsigma[row] = rs;
       if constexpr (NORM == NT_LAYERNORM) {
@@ -149,12 +209,13 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
     for (int k = 0; k < KC; ++k) {
       const bool ok = rv && cv[k];
       const int64_t col = 8 * (int64_t)(tl + TEAM * k);
-      float xv[8], y[8];
-      strip_to_f32<IN>(xs[k], xv);
+      float gk[8], bk[8], xv[8], y[8];
+      weights(k, gk, bk);
+      strip_to_f32<IN>(cur[k], xv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if constexpr (NORM == NT_LAYERNORM) y[i] = fmaf((xv[i] - mu) * rs, g[k][i], b[k][i]);
-        else y[i] = (xv[i] * rs) * g[k][i];
+        if constexpr (NORM == NT_LAYERNORM) y[i] = fmaf((xv[i] - mu) * rs, gk[i], bk[i]);
+        else y[i] = (xv[i] * rs) * gk[i];
       }
       if constexpr (MODE == MODE_PLAIN) {
         if (ok) store_out8(p.y, row * H + col, y, fmt);
@@ -185,23 +246,30 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
         }
       }
     }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) cur[k] = nxt[k];
   }
 
   if constexpr (MODE == MODE_DELAYED) {
-    // tensor amax: wave max -> one atomic max per wave -> the last workgroup to finish
-    // publishes max(amax_in, amax) and re-zeroes the header words it used
+    // tensor amax: workgroup max -> this workgroup's tagged slot; the last workgroup to finish
+    // takes the max over all slots, publishes max(amax_in, amax) and re-zeroes the counters
+    __shared__ float wred[P * T];
+    __shared__ uint32_t last_flag;
     const float m = wave_max(amax_local);
-    if (lane == 0) max_dev(p.ws + kWsAmax, __float_as_uint(m));
-    vmem_drain();
+    if (lane == 0) wred[wave] = m;
     __syncthreads();
     if (tid == 0) {
-      const uint32_t prev = add_dev(p.ws + kWsDone, 1u);
-      if (prev == gridDim.x - 1) {
-        const float tot = __uint_as_float(xchg_dev(p.ws + kWsAmax, 0u));
-        *p.updated_amax = fmaxf(*p.amax_in, tot);
-        xchg_dev(p.ws + kWsDone, 0u);
-      }
+      float a = wred[0];
+#pragma unroll
+      for (int w = 1; w < P * T; ++w) a = fmaxf(a, wred[w]);
+      publish_amax(p.ws, a, tag);
       if (blockIdx.x == 0) *static_cast<float *>(p.scale_inv) = 1.0f / scale;
+    }
+    vmem_drain();
+    if (finish_workgroup(p.ws, &last_flag)) {
+      const float tot = gather_amax(p.ws, gridDim.x, wred, tag);
+      if (tid == 0) *p.updated_amax = fmaxf(*p.amax_in, tot);
+      reset_completion(p.ws);
     }
   }
 }
@@ -210,21 +278,28 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
 // instantiation table
 // ------------------------------------------------------------------------------------------
 
+// weights go to LDS when the team's cover of float32 gamma (and beta) fits in 64 KB
+template <int NORM, int P, int KC> constexpr int wl_for() {
+  return (NORM == NT_LAYERNORM ? 2 : 1) * 8 * 64 * P * KC * 4 <= 65536 && KC >= 4 ? 1 : 0;
+}
+
 template <int NORM, class IN, int MODE>
 static const void *pick_cfg(int cfg) {
+#define NF8_ROW(P, T, KC) (const void *)fwd_row_kernel<NORM, IN, MODE, P, T, KC, wl_for<NORM, P, KC>()>
   switch (cfg) {
-    case ROW_W1_K1: return (const void *)fwd_row_kernel<NORM, IN, MODE, 1, 4, 1>;
-    case ROW_W1_K2: return (const void *)fwd_row_kernel<NORM, IN, MODE, 1, 4, 2>;
-    case ROW_W1_K4: return (const void *)fwd_row_kernel<NORM, IN, MODE, 1, 4, 4>;
-    case ROW_W1_K8: return (const void *)fwd_row_kernel<NORM, IN, MODE, 1, 4, 8>;
-    case ROW_W4_K2: return (const void *)fwd_row_kernel<NORM, IN, MODE, 4, 1, 2>;
-    case ROW_W4_K4: return (const void *)fwd_row_kernel<NORM, IN, MODE, 4, 1, 4>;
-    case ROW_W8_K4: return (const void *)fwd_row_kernel<NORM, IN, MODE, 8, 1, 4>;
-    case ROW_W2T2_K4: return (const void *)fwd_row_kernel<NORM, IN, MODE, 2, 2, 4>;
-    case ROW_W8_K1: return (const void *)fwd_row_kernel<NORM, IN, MODE, 8, 1, 1>;
-    case ROW_W4T2_K2: return (const void *)fwd_row_kernel<NORM, IN, MODE, 4, 2, 2>;
+    case ROW_W1_K1: return NF8_ROW(1, 4, 1);
+    case ROW_W1_K2: return NF8_ROW(1, 4, 2);
+    case ROW_W1_K4: return NF8_ROW(1, 4, 4);
+    case ROW_W1_K8: return NF8_ROW(1, 4, 8);
+    case ROW_W4_K2: return NF8_ROW(4, 1, 2);
+    case ROW_W4_K4: return NF8_ROW(4, 1, 4);
+    case ROW_W8_K4: return NF8_ROW(8, 1, 4);
+    case ROW_W2T2_K4: return NF8_ROW(2, 2, 4);
+    case ROW_W8_K1: return NF8_ROW(8, 1, 1);
+    case ROW_W4T2_K2: return NF8_ROW(4, 2, 2);
     default: return nullptr;
   }
+#undef NF8_ROW
 }
 
 template <int NORM, class IN>

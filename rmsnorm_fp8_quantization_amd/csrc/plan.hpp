@@ -23,17 +23,29 @@ enum : int { MODE_PLAIN = 0, MODE_DELAYED = 1, MODE_MX = 2 };
 constexpr uint64_t kSpinLimitTicks = 200000000ull;
 
 // ---- workspace header (NORM_WS_HEADER_BYTES at offset 0 of every workspace) --------------
-// All words are zero between calls. `done` counts finished workgroups; the workgroup that
-// finishes last publishes the per-call results (updated amax) and re-zeroes the header.
+// Counters are zero between calls. A launch that coordinates workgroups counts finished
+// workgroups in two levels (64 per group counter, then one counter of finished groups) so no
+// word takes more than 64 atomic updates; the workgroup that finishes last publishes the
+// per-call results (updated amax), re-zeroes the counters and advances the epoch.
+//
+// Values that cross workgroups are 64-bit words {value bits, tag} written with one 64-bit
+// store; tag = epoch + 1 of the writing launch. A reader polls the words it needs until their
+// tag is its own launch's, so it never depends on the order in which two different addresses
+// become visible, and a word left by an earlier launch (or a zero-filled workspace) is never
+// mistaken for a current one.
 constexpr int kWsHeaderBytes = 16384;
-constexpr int kWsDone = 0;      // u32: finished workgroups of the current launch
-constexpr int kWsTicket = 1;    // u32: band-tile tickets handed out in the current launch
-constexpr int kWsAmax = 2;      // u32: float bits of max |y| of the current launch
-constexpr int kWsError = 3;     // u32: sticky error flags (bit 0: a wait timed out)
-constexpr int kWsSlot0 = 16;    // first band-arrival slot counter
-constexpr int kWsSlots = kWsHeaderBytes / 4 - kWsSlot0;  // 4080 slot counters
+constexpr int kWsDone = 0;        // u32: finished groups of workgroups
+constexpr int kWsError = 1;       // u32: sticky error flags (bit 0: a wait timed out)
+constexpr int kWsEpoch = 2;       // u32: launches completed on this workspace (tags = epoch + 1)
+constexpr int kWsTicket0 = 8;     // u32[8]: tile tickets handed out, one counter per class
+constexpr int kWsGroup0 = 16;     // u32[32]: finished workgroups per group of 64 (up to word 47)
+constexpr int kWsAmax0 = 48;      // u64[kMaxGrid]: per-workgroup {max |y|, tag} (delayed scaling)
+constexpr int kWsGroupSize = 64;
+constexpr int kMaxGrid = 2016;    // largest persistent grid (bounded by the header's arrays)
+constexpr int kClasses = 8;       // ticket classes (one per XCD of the MI355X)
 // most workgroups one band may be split over (bounds the LDS used to merge their partials)
 constexpr int kMaxSlices = 64;
+static_assert(kWsAmax0 * 4 + kMaxGrid * 8 <= kWsHeaderBytes, "header overflow");
 
 // ---- forward row kernel --------------------------------------------------------------------
 // A team of P waves normalises one row at a time; a workgroup holds T teams; each lane owns
@@ -68,10 +80,12 @@ struct FwdBandParams {
   FwdRowParams f;        // shared fields (y = rowwise output or nullptr)
   void *y_col;           // [hidden, rows] columnwise codes or nullptr
   void *col_scale_inv;   // delayed: float32[1]; MX: uint8 [hidden, ceil(rows/32)]
-  float *partials;       // [bands, S, R, 2] per-row partial statistics (S > 1)
+  uint64_t *partials;    // [bands, S, R, NV] tagged per-row partial statistics (S > 1);
+                         // NV = 2 (mean, M2) for LayerNorm, 1 (sum of squares) for RMSNorm
   int64_t bands;         // ceil(rows / R)
   int64_t mx_rows;       // ceil(rows / 32)
   int S;                 // workgroups per band
+  int classes;           // ticket classes (1 or kClasses); gridDim.x is a multiple of it
   int write_row;         // rowwise output requested
 };
 

@@ -10,7 +10,7 @@ Tolerances (written here, used by every parity test):
   FP8 codes       ordered code distance <= 1; at most 0.1% of elements differ; each
                   differing element's exact scaled value lies within 1e-5 (relative) of
                   the midpoint between the two codes' values, i.e. on a rounding boundary
-  E8M0 scales     bit-exact, except blocks whose float64 maximum lies within 2^-21
+  E8M0 scales     bit-exact, except blocks whose float64 maximum lies within 2^-19
                   (relative) of a power of two, where the binary32 maximum may fall on
                   either side: there either neighbouring exponent is accepted and the
                   block's codes are checked under the GPU's exponent
@@ -28,8 +28,11 @@ import numpy as np
 import oracle
 from oracle import formats as F
 
+# e8m0_window: the binary32 kernel reaches a block maximum through a tree sum of squares over
+# the row ((log2 H + 1) * 2^-24 relative at H = 12288 is ~9e-7, half of it in rsigma) and
+# three roundings of y, ~2^-20 together; 2^-19 bounds it.
 TOL = dict(mu=1e-5, rsigma=1e-5, f32=1e-5, dx16=2e-3, wgrad=1e-4, amax=1e-6, fp8_frac=1e-3,
-           fp8_tau=1e-5, e8m0_window=2.0 ** -21)
+           fp8_tau=1e-5, e8m0_window=2.0 ** -19)
 
 
 class Report(dict):
@@ -99,7 +102,13 @@ def check_fp8(codes_g: np.ndarray, codes_ref: np.ndarray, u_exact: np.ndarray, f
     dist = np.abs(og - orf)
     # +0 / -0 are the same value
     zero_pair = (F.fp8_decode(cg[diff], fmt) == 0) & (F.fp8_decode(cr[diff], fmt) == 0)
-    assert np.all((dist[diff] <= 1) | zero_pair), f"{what}: codes more than one step apart"
+    far = ~((dist[diff] <= 1) | zero_pair)
+    if far.any():
+        idx = np.argwhere(diff)[far][:6]
+        raise AssertionError(
+            f"{what}: {int(far.sum())} codes more than one step apart at {idx.tolist()}: gpu "
+            f"{[hex(int(cg[tuple(i)])) for i in idx]} oracle {[hex(int(cr[tuple(i)])) for i in idx]} "
+            f"exact scaled {[float(np.asarray(u_exact)[tuple(i)]) for i in idx]}")
     frac = n / cg.size
     assert frac <= TOL["fp8_frac"], f"{what}: {n} of {cg.size} codes differ ({frac:.2e})"
     vg = F.fp8_decode(cg[diff], fmt)
@@ -151,8 +160,13 @@ def check_mx_rows(codes_g, scales_g, v, fp8, what="mx"):
             k = np.floor(np.log2(np.where(a64 > 0, a64, 1.0)))
             near = (np.abs(a64 - 2.0 ** k) <= TOL["e8m0_window"] * a64) | \
                    (np.abs(a64 - 2.0 ** (k + 1)) <= TOL["e8m0_window"] * a64)
-            assert np.all(near[bad] & (np.abs(x_g - x_ref)[bad] == 1)), \
-                f"{what}: {int(bad.sum())} E8M0 scales differ away from a power-of-two boundary"
+            if not np.all(near[bad] & (np.abs(x_g - x_ref)[bad] == 1)):
+                kk = k[bad]
+                dist = np.minimum(np.abs(a64[bad] - 2.0 ** kk), np.abs(a64[bad] - 2.0 ** (kk + 1))) / a64[bad]
+                raise AssertionError(
+                    f"{what} block {b}: {int(bad.sum())} E8M0 scales differ: rows {np.nonzero(bad)[0][:8]}, "
+                    f"gpu X {x_g[bad][:8]}, oracle X {x_ref[bad][:8]}, block max {a64[bad][:8]}, "
+                    f"relative distance to a power of two {dist[:8]}")
             boundary += int(bad.sum())
         scaled = blk32 * np.ldexp(1.0, -x_g)[:, None]
         ref_codes = F.fp8_quantize(F.round_nearest_even(scaled, F.FP32), fmt)
