@@ -120,7 +120,9 @@ struct FwdPlan {
   int mode = MODE_PLAIN;
   bool rowwise = true, colwise = false;
   bool band = false;
+  bool col = false;  // band layout served by the 128-row columnwise kernel
   int cfg = 0;
+  int tile_rows = 0;  // rows per band
   int S = 1;
   int64_t bands = 0;
   size_t ws_bytes = 0;
@@ -175,6 +177,7 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     pl->cfg = row_cfg;
   } else {
     int bc;
+    pl->col = pl->colwise && env_int("NORMFP8_COL_KERNEL", 1) != 0;
     if (pl->colwise) bc = hidden <= 512 ? BAND_R8_K1 : BAND_R8_K2;
     else bc = hidden <= 2048 ? BAND_R1_K4 : BAND_R2_K8;
     const int band_override = env_int("NORMFP8_BAND_CFG", -1);
@@ -183,8 +186,9 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
         !(pl->colwise && pl->mode == MODE_MX && kBandShapes[band_override].RW != 8))
       bc = band_override;
     pl->cfg = bc;
-    pl->S = (int)cdiv(hidden, kBandShapes[bc].cols());
-    pl->bands = cdiv(rows, kBandShapes[bc].rows());
+    pl->tile_rows = pl->col ? kColTileRows : kBandShapes[bc].rows();
+    pl->S = (int)cdiv(hidden, pl->col ? kColTileCols : kBandShapes[bc].cols());
+    pl->bands = cdiv(rows, pl->tile_rows);
     if (pl->S > kMaxSlices)
       return fail(NORM_ERR_UNSUPPORTED, "hidden %lld needs %d workgroups per band; this build allows %d",
                   (long long)hidden, pl->S, kMaxSlices);
@@ -196,7 +200,7 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   if (pl->band && pl->S > 1) {
     pl->partial_off = ws;
     const int nv = norm_type == NORM_LAYERNORM ? 2 : 1;
-    ws += round_up((size_t)pl->bands * pl->S * kBandShapes[pl->cfg].rows() * nv * sizeof(uint64_t), 256);
+    ws += round_up((size_t)pl->bands * pl->S * pl->tile_rows * nv * sizeof(uint64_t), 256);
   }
   pl->ws_bytes = ws;
   (void)in_dtype;
@@ -388,12 +392,14 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   b.mx_rows = cdiv(rows, 32);
   b.S = pl.S;
   b.write_row = pl.rowwise ? 1 : 0;
-  const void *fn = fwd_band_kernel_ptr(norm_type, in_dtype, pl.mode, pl.colwise, pl.cfg);
+  const void *fn = pl.col ? fwd_col_kernel_ptr(norm_type, in_dtype, pl.mode)
+                          : fwd_band_kernel_ptr(norm_type, in_dtype, pl.mode, pl.colwise, pl.cfg);
   if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no forward band kernel for this combination");
+  const int threads = pl.col ? kColThreads : 256;
   // persistent grid: at most what fits on the CUs left by the margin; the S workgroups of a
   // band wait for each other, so at least S must be able to run at once
   int occ = 1;
-  rc = occupancy(fn, 256, &occ);
+  rc = occupancy(fn, threads, &occ);
   if (rc) return rc;
   int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
   if (cap > kMaxGrid) cap = kMaxGrid;
@@ -409,7 +415,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     b.classes = kClasses;
     grid = grid / kClasses * kClasses;
   }
-  rc = launch(fn, dim3((unsigned)grid), dim3(256), &b, st);
+  rc = launch(fn, dim3((unsigned)grid), dim3(threads), &b, st);
   if (rc) return rc;
   return ok();
 }

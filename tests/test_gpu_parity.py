@@ -58,12 +58,20 @@ def oracle_fwd(case, norm, in_dt, w_dt, zc):
                                  norm=norm, eps=EPS, in_dtype=in_dt, w_dtype=w_dt, zero_centered_gamma=zc)
 
 
-def ln_terms(case, ref, norm, w_dt="f32"):
-    """|xhat * g| + |beta| per element (LayerNorm), the magnitude of the summed terms."""
+def ln_terms(case, ref, norm, w_dt="f32", zc=False):
+    """|xhat * g| + |mu * rsigma * g| + |beta| per element (LayerNorm): the magnitude of the
+    terms whose binary32 sum gives y (x * rsigma * g, the mean's share, beta)."""
     if norm != "layernorm":
         return None
     beta = F.decode_storage(host_np(case["beta"], w_dt), w_dt)[None, :]
-    return np.abs(ref["v"] - beta) + np.abs(beta)
+    g = oracle.effective_gamma(F.decode_storage(host_np(case["gamma"], w_dt), w_dt), zc)[None, :]
+    mu_share = np.abs(ref["mu"][:, None] * ref["rsigma"][:, None] * g)
+    return np.abs(ref["v"] - beta) + mu_share + np.abs(beta)
+
+
+def T(a):
+    """Transpose of a per-element array (None stays None)."""
+    return None if a is None else np.ascontiguousarray(a.T)
 
 
 def gpu(case, *names):
@@ -171,7 +179,7 @@ def test_fwd_delayed(fp8, layout, norm, rows, hidden):
            "colwise_scale_inv": out["colwise_scale_inv"].item() if out["colwise_scale_inv"] is not None else None,
            "amax": out["amax"].item()}
     checks.check_delayed(got, ref["v"], scale, 0.25, fp8, rowwise=layout != "colwise",
-                         colwise=layout != "rowwise")
+                         colwise=layout != "rowwise", terms=ln_terms(case, ref, norm))
     checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
                        out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
     assert_ws_clean()
@@ -204,11 +212,12 @@ def test_fwd_mxfp8(fp8, layout, norm, rows, hidden, zc):
     ref = oracle_fwd(case, norm, "bf16", "f32", zc)
     x, g, b = gpu(case, "x", "gamma", "beta")
     out = nf.fwd(x, g, b, norm=norm, eps=EPS, zero_centered_gamma=zc, scaling="mxfp8", fp8=fp8, layout=layout)
+    t = ln_terms(case, ref, norm, zc=zc)
     if layout != "colwise":
-        checks.check_mx_rows(bits(out["y"]), bits(out["scale_inv"]), ref["v"], fp8, "mx rowwise")
+        checks.check_mx_rows(bits(out["y"]), bits(out["scale_inv"]), ref["v"], fp8, "mx rowwise", terms=t)
     if layout != "rowwise":
         checks.check_mx_rows(bits(out["y_colwise"]), bits(out["colwise_scale_inv"]),
-                             np.ascontiguousarray(ref["v"].T), fp8, "mx colwise")
+                             np.ascontiguousarray(ref["v"].T), fp8, "mx colwise", terms=T(t))
     checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
                        out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
     assert_ws_clean()
@@ -224,7 +233,93 @@ def test_fwd_mxfp8_zero_block():
     sc = bits(out["scale_inv"])
     assert np.all(sc[:, 0] == 0) and np.all(bits(out["y"])[:, :32] == 0)
     checks.check_mx_rows(bits(out["y_colwise"]), bits(out["colwise_scale_inv"]),
-                         np.ascontiguousarray(ref["v"].T), "e4m3", "mx colwise")
+                         np.ascontiguousarray(ref["v"].T), "e4m3", "mx colwise", terms=T(ln_terms(case, ref, "layernorm")))
+
+
+# ------------------------------------------------------------------------------ columnwise tiles
+
+# (rows, hidden): one tile, ragged rows (N % 16 != 0 and N % 128 != 0), hidden not a multiple
+# of 512 or of 32, bands split over up to 40 workgroups, and sizes that enable ticket classes
+COL_SHAPES = [(1, 8), (128, 512), (45, 1000), (300, 4104), (130, 8192), (2, 20480), (4096, 512),
+              (4096, 2048)]
+
+
+@pytest.mark.parametrize("scaling", ["delayed", "mxfp8"])
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("rows,hidden", COL_SHAPES)
+def test_fwd_colwise_tiles(scaling, norm, rows, hidden):
+    case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=rows * 7 + hidden)
+    ref = oracle_fwd(case, norm, "bf16", "f32", False)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    if scaling == "delayed":
+        scale = float(np.float32(448.0) / np.float32(np.max(np.abs(ref["v"]))))
+        st = torch.tensor([scale], device="cuda")
+        out = nf.fwd(x, g, b, norm=norm, eps=EPS, scaling="delayed", scale=st, amax=torch.zeros(1, device="cuda"),
+                     layout="rowwise_colwise")
+        got = {"y": bits(out["y"]), "y_colwise": bits(out["y_colwise"]), "scale_inv": out["scale_inv"].item(),
+               "colwise_scale_inv": out["colwise_scale_inv"].item(), "amax": out["amax"].item()}
+        checks.check_delayed(got, ref["v"], scale, 0.0, "e4m3", rowwise=True, colwise=True,
+                             terms=ln_terms(case, ref, norm))
+    else:
+        out = nf.fwd(x, g, b, norm=norm, eps=EPS, scaling="mxfp8", layout="rowwise_colwise")
+        t = ln_terms(case, ref, norm)
+        checks.check_mx_rows(bits(out["y"]), bits(out["scale_inv"]), ref["v"], "e4m3", "mx rowwise", terms=t)
+        checks.check_mx_rows(bits(out["y_colwise"]), bits(out["colwise_scale_inv"]),
+                             np.ascontiguousarray(ref["v"].T), "e4m3", "mx colwise", terms=T(t))
+    checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
+                       out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+    assert_ws_clean()
+
+
+@pytest.mark.parametrize("in_dt", ["f32", "f16"])
+@pytest.mark.parametrize("layout", ["colwise", "rowwise_colwise"])
+def test_fwd_colwise_other_input_dtypes(in_dt, layout):
+    case = workloads.small_case("layernorm", 200, 1536, in_dt, "bf16", seed=11)
+    ref = oracle_fwd(case, "layernorm", in_dt, "bf16", False)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    out = nf.fwd(x, g, b, norm="layernorm", eps=EPS, scaling="mxfp8", fp8="e5m2", layout=layout)
+    t = ln_terms(case, ref, "layernorm", "bf16")
+    if layout != "colwise":
+        checks.check_mx_rows(bits(out["y"]), bits(out["scale_inv"]), ref["v"], "e5m2", "mx rowwise", terms=t)
+    checks.check_mx_rows(bits(out["y_colwise"]), bits(out["colwise_scale_inv"]),
+                         np.ascontiguousarray(ref["v"].T), "e5m2", "mx colwise", terms=T(t))
+    checks.check_stats(out["mu"].cpu().numpy(), out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+    assert_ws_clean()
+
+
+@pytest.mark.parametrize("classes", [1, 8])
+def test_fwd_colwise_classes_and_repeats(classes):
+    """Ticket classes on and off; consecutive launches reuse the workspace (tags, tickets)."""
+    case = workloads.small_case("rmsnorm", 4096, 1024, "bf16", "f32", seed=5)
+    ref = oracle_fwd(case, "rmsnorm", "bf16", "f32", False)
+    x, g = gpu(case, "x", "gamma")
+    with env(NORMFP8_BAND_CLASSES=classes):
+        for _ in range(3):
+            out = nf.fwd(x, g, None, norm="rmsnorm", eps=EPS, scaling="mxfp8", layout="rowwise_colwise")
+            checks.check_mx_rows(bits(out["y_colwise"]), bits(out["colwise_scale_inv"]),
+                                 np.ascontiguousarray(ref["v"].T), "e4m3", "mx colwise")
+    assert_ws_clean()
+
+
+@pytest.mark.parametrize("scaling", ["delayed", "mxfp8"])
+def test_fwd_colwise_32_row_band_kernel(scaling):
+    """The 32-row band kernel's columnwise path (selected with NORMFP8_COL_KERNEL=0)."""
+    case = workloads.small_case("rmsnorm", 100, 2056, "bf16", "f32", seed=3)
+    ref = oracle_fwd(case, "rmsnorm", "bf16", "f32", False)
+    x, g = gpu(case, "x", "gamma")
+    with env(NORMFP8_COL_KERNEL=0):
+        if scaling == "delayed":
+            scale = float(np.float32(448.0) / np.float32(np.max(np.abs(ref["v"]))))
+            out = nf.fwd(x, g, None, norm="rmsnorm", eps=EPS, scaling="delayed", layout="rowwise_colwise",
+                         scale=torch.tensor([scale], device="cuda"), amax=torch.zeros(1, device="cuda"))
+            got = {"y": bits(out["y"]), "y_colwise": bits(out["y_colwise"]), "scale_inv": out["scale_inv"].item(),
+                   "colwise_scale_inv": out["colwise_scale_inv"].item(), "amax": out["amax"].item()}
+            checks.check_delayed(got, ref["v"], scale, 0.0, "e4m3", rowwise=True, colwise=True)
+        else:
+            out = nf.fwd(x, g, None, norm="rmsnorm", eps=EPS, scaling="mxfp8", layout="rowwise_colwise")
+            checks.check_mx_rows(bits(out["y_colwise"]), bits(out["colwise_scale_inv"]),
+                                 np.ascontiguousarray(ref["v"].T), "e4m3", "mx colwise")
+    assert_ws_clean()
 
 
 # ------------------------------------------------------------------------------ backward
@@ -310,13 +405,15 @@ def test_fwd_then_bwd_end_to_end():
 def test_repeat_runs_are_bitwise_identical():
     case = workloads.small_case("layernorm", 500, 20480, "bf16", "f32", seed=8)
     dy, x, g, b = gpu(case, "dy", "x", "gamma", "beta")
+    xs, dys, gs = x[:, :16384].contiguous(), dy[:, :16384].contiguous(), g[:16384].contiguous()
     outs = []
     for _ in range(3):
-        f = nf.fwd(x, g, b, norm="layernorm")
-        d = nf.bwd(dy, x[:, :16384].contiguous(), f["mu"], f["rsigma"], g[:16384].contiguous(), norm="layernorm")
-        outs.append((f["y"].clone(), f["mu"].clone(), d["dx"].clone(), d["dgamma"].clone(), d["dbeta"].clone()))
+        f = nf.fwd(x, g, b, norm="layernorm")                      # band split (20480 columns)
+        fc = nf.fwd(x, g, b, norm="layernorm", scaling="mxfp8", layout="rowwise_colwise")
+        d = nf.bwd(dys, xs, f["mu"], f["rsigma"], gs, norm="layernorm")
+        outs.append([t.clone() for t in (f["y"], f["mu"], fc["y"], fc["y_colwise"], fc["colwise_scale_inv"],
+                                          d["dx"], d["dgamma"], d["dbeta"])])
     for o in outs[1:]:
         for a, b_ in zip(outs[0], o):
-            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a, b_.view(torch.uint8)
-                               if b_.dtype == torch.bfloat16 else b_)
+            assert torch.equal(a.view(torch.uint8), b_.view(torch.uint8))
     assert_ws_clean()
