@@ -17,6 +17,7 @@ call (the backward) against the 8 TB/s HBM peak, timed with HIP events on the la
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -181,36 +182,93 @@ def run_workload(w: W.Workload, nf, steps: int, warmup: int, headline: bool):
     return res
 
 
+# ------------------------------------------------------------------------------ HBM traffic
+
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.txt")
+BWD_SOURCES = ["rmsnorm_fp8_quantization_amd/csrc/bwd.hip", "rmsnorm_fp8_quantization_amd/csrc/device_common.hpp",
+               "rmsnorm_fp8_quantization_amd/csrc/plan.hpp", "rmsnorm_fp8_quantization_amd/csrc/api.cpp"]
+
+
+def sources_sha256(paths):
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per backward call from the committed rocprofv3 counter summary, scaled by the
+    copy-kernel calibration recorded with it; None when the summary is missing or the backward
+    sources have changed since the counters were taken."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    with open(COUNTERS) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if kv.get("bwd_sources_sha256") != sources_sha256(BWD_SOURCES):
+            return None
+        return float(kv["bwd_call_hbm_bytes"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
+    """A plain device copy of known size (run under rocprofv3 --pmc to calibrate FETCH_SIZE and
+    WRITE_SIZE): prints its bytes and mean time."""
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
+                      "us_per_copy": dt * 1e6, "GBps": 2 * nbytes / dt / 1e9}))
+
+
 # ------------------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(w: W.Workload, budget_s: float = 15.0):
-    """Oracle (float64 numpy) on the first rows of the workload's batch, growing the sample
-    until it takes at least ~budget_s / 2; reported in the metric's unit (GB/s)."""
+def cpu_baseline(w: W.Workload, min_s: float = 10.0, max_passes: int = 8):
+    """The float64 oracle (numpy, one thread) on the workload's whole batch, forward + backward,
+    in chunks of 4096 rows, repeated until at least `min_s` seconds of CPU work (bounded by
+    `max_passes` passes); reported in the metric's unit (GB/s over the same byte model)."""
     import oracle
-    host = W.make_inputs(w.scaled(rows=min(w.rows, 4096)))
+    host = W.make_inputs(w)
     xb = W.to_numpy_bits(host["x"])
     dyb = W.to_numpy_bits(host["dy"]) if "dy" in host else None
     g = W.to_numpy_bits(host["gamma"])
     b = W.to_numpy_bits(host["beta"]) if "beta" in host else None
-    rows = 64
+    del host
+    chunk = 4096
+    passes = 0
+    t0 = time.perf_counter()
     while True:
-        t0 = time.perf_counter()
-        f = oracle.forward_stored(xb[:rows], g, b, norm=w.norm, eps=w.eps, in_dtype=w.in_dtype,
-                                  w_dtype=w.w_dtype, zero_centered_gamma=w.zero_centered_gamma)
-        oracle.plain_output(f["v"], w.in_dtype)
-        if dyb is not None:
-            oracle.backward_stored(dyb[:rows], xb[:rows], f["mu"], f["rsigma"], g, norm=w.norm,
-                                   in_dtype=w.in_dtype, w_dtype=w.w_dtype,
-                                   zero_centered_gamma=w.zero_centered_gamma)
+        for r0 in range(0, w.rows, chunk):
+            sl = slice(r0, min(w.rows, r0 + chunk))
+            f = oracle.forward_stored(xb[sl], g, b, norm=w.norm, eps=w.eps, in_dtype=w.in_dtype,
+                                      w_dtype=w.w_dtype, zero_centered_gamma=w.zero_centered_gamma)
+            oracle.plain_output(f["v"], w.in_dtype)
+            if dyb is not None:
+                oracle.backward_stored(dyb[sl], xb[sl], f["mu"], f["rsigma"], g, norm=w.norm,
+                                       in_dtype=w.in_dtype, w_dtype=w.w_dtype,
+                                       zero_centered_gamma=w.zero_centered_gamma)
+        passes += 1
         dt = time.perf_counter() - t0
-        if dt >= budget_s / 2 or rows >= xb.shape[0]:
+        if dt >= min_s or passes >= max_passes:
             break
-        rows = min(xb.shape[0], rows * 2)
-    sw = w.scaled(rows=rows)
-    nbytes = fwd_bytes(sw) + (bwd_bytes(sw, False) if dyb is not None else 0)
+    nbytes = passes * (fwd_bytes(w) + (bwd_bytes(w, False) if dyb is not None else 0))
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} of {w.rows} rows of one {w.name} batch, fwd+bwd, float64 numpy "
-                      f"({dt:.2f} s)", "rows_per_s": rows / dt}
+            "sample": f"{passes} pass(es) over the whole {w.name} batch ({w.rows} rows), fwd+bwd, "
+                      f"float64 numpy on one thread, {dt:.1f} s",
+            "rows_per_s": passes * w.rows / dt}
 
 
 # ------------------------------------------------------------------------------ main
@@ -222,6 +280,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for rocprofv3 counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the method shards by rows "
@@ -230,9 +290,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import rmsnorm_fp8_quantization_amd as nf
 
-    torch.cuda.set_device(0)
     hw = W.WORKLOADS[HEADLINE]
     head = run_workload(hw, nf, args.steps, args.warmup, True)
     print(f"[bench] {HEADLINE}: step {head['step_ms']*1e3:.1f} us, {head['GBps']:.0f} GB/s", file=sys.stderr,
@@ -270,7 +333,7 @@ def main():
                    "in_dtype": hw.in_dtype, "w_dtype": hw.w_dtype, "eps": hw.eps,
                    "step": "fwd(batch k) + bwd(batch k-1)"},
         "roofline": {"bound": "hbm", "achieved": round(bwd["GBps"], 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(bwd["GBps"] / PEAK_GBS, 4), "traffic": None,
+                     "frac": round(bwd["GBps"] / PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "norm_bwd (bwd_kernel + bwd_finalize_kernel)",
                      "bytes_per_launch": bwd["bytes"], "us_per_launch": round(bwd["us_mean"], 2)},
         "cpu_baseline": cpu,
