@@ -79,11 +79,30 @@ template <class T> __device__ __forceinline__ void opaque(Strip<T> &s) {
     asm volatile("" : "+v"(s.v[i].x), "+v"(s.v[i].y), "+v"(s.v[i].z), "+v"(s.v[i].w));
 }
 
+// Streaming accesses: every input row element is read once and every output element written
+// once, so rows use non-temporal loads and stores (they do not displace reused data such as the
+// weights from the caches; on MI355X they also raise the achieved HBM bandwidth of a stream).
+typedef unsigned int nf8_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nf8_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_nt16(const void *p) {
+  const nf8_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nf8_u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt16(void *p, uint4 v) {
+  const nf8_u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<nf8_u32x4 *>(p));
+}
+__device__ __forceinline__ void st_nt8(void *p, uint2 v) {
+  const nf8_u32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<nf8_u32x2 *>(p));
+}
+
+// one strip of a row (non-temporal)
 template <class T>
 __device__ __forceinline__ void load_strip(Strip<T> &s, const void *base, int64_t elem) {
-  const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + elem * T::bytes);
+  const char *p = static_cast<const char *>(base) + elem * T::bytes;
 #pragma unroll
-  for (int i = 0; i < (int)(sizeof(Strip<T>) / 16); ++i) s.v[i] = p[i];
+  for (int i = 0; i < (int)(sizeof(Strip<T>) / 16); ++i) s.v[i] = ld_nt16(p + 16 * i);
 }
 template <class T> __device__ __forceinline__ void zero_strip(Strip<T> &s) {
 #pragma unroll
@@ -97,8 +116,8 @@ __device__ __forceinline__ void load_w8(float (&o)[8], const void *base, int64_t
     float4 a = p[0], b = p[1];
     o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
   } else {
-    Strip<BF16> s;
-    load_strip<BF16>(s, base, elem);
+    Strip<BF16> s;  // cached: the weights are reused by every row
+    s.v[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
     if (dt == DT_BF16) {
       strip_to_f32<BF16>(s, o);
     } else {
@@ -121,17 +140,17 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 // store 8 float32 values as runtime out dtype (F32 / F16 / BF16) at element offset `elem`
 __device__ __forceinline__ void store_out8(void *base, int64_t elem, const float (&y)[8], int dt) {
   if (dt == DT_F32) {
-    float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(base) + elem);
-    p[0] = make_float4(y[0], y[1], y[2], y[3]);
-    p[1] = make_float4(y[4], y[5], y[6], y[7]);
+    float *p = static_cast<float *>(base) + elem;
+    st_nt16(p, make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])));
+    st_nt16(p + 4, make_uint4(__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7])));
   } else if (dt == DT_BF16) {
-    uint4 *p = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + elem);
-    *p = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                    pack_bf16x2(y[6], y[7]));
+    st_nt16(static_cast<uint16_t *>(base) + elem,
+            make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                       pack_bf16x2(y[6], y[7])));
   } else {
-    uint4 *p = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + elem);
-    *p = make_uint4(pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]), pack_f16x2(y[4], y[5]),
-                    pack_f16x2(y[6], y[7]));
+    st_nt16(static_cast<uint16_t *>(base) + elem,
+            make_uint4(pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]), pack_f16x2(y[4], y[5]),
+                       pack_f16x2(y[6], y[7])));
   }
 }
 

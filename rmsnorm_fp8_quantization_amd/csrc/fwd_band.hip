@@ -62,7 +62,7 @@ __device__ __forceinline__ void store_col_codes(const uint2 (&codes)[RW], uint8_
       const uint32_t w0 = i < 4 ? lo[0][i] : hi[0][i - 4];
       if constexpr (RW == 8) {
         const uint32_t w1 = i < 4 ? lo[1][i] : hi[1][i - 4];
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(w0, w1);
+        st_nt8(dst, make_uint2(w0, w1));
       } else {
         *reinterpret_cast<uint32_t *>(dst) = w0;
       }
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
           }
           rcodes[j] = fp8_pack8(u, fmt);
           if (ok && bp.write_row)
-            *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.y) + row * H + col) = rcodes[j];
+            st_nt8(static_cast<uint8_t *>(p.y) + row * H + col, rcodes[j]);
         } else {  // MX
           if (bp.write_row) {
             float a = 0.0f;
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
             for (int i = 0; i < 8; ++i) u[i] = y[i] * f;
             const uint2 c = fp8_pack8(u, fmt);
             if (ok) {
-              *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.y) + row * H + col) = c;
+              st_nt8(static_cast<uint8_t *>(p.y) + row * H + col, c);
               if ((lane & 3) == 0)
                 static_cast<uint8_t *>(p.scale_inv)[row * p.mx_cols + (col >> 5)] = (uint8_t)(X + 127);
             }

@@ -25,7 +25,8 @@ namespace nf8 {
 // WL: where the weights live while the workgroup walks its rows. 0: each lane keeps its
 // columns' gamma / beta in registers; 1: the workgroup stages them once in LDS (as float32,
 // 1 + gamma when zero-centred), leaving the registers to the row data so that the next row
-// can be in flight while the current one is normalised.
+// can be in flight while the current one is normalised; 2 (rows too long for either): each
+// strip's weights are read where they are used (they stay in the L2 across rows).
 template <int NORM, class IN, int MODE, int P, int T, int KC, int WL>
 __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   constexpr int TEAM = 64 * P;
@@ -46,10 +47,12 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   for (int k = 0; k < KC; ++k) cv[k] = 8 * (int64_t)(tl + TEAM * k) < H;
 
   // ---- weights
-  __shared__ float wlds[WL ? NW * COVER : 1];
+  __shared__ float wlds[WL == 1 ? NW * COVER : 1];
   float g[WL ? 1 : KC][8];
   float b[(!WL && NORM == NT_LAYERNORM) ? KC : 1][8];
-  if constexpr (WL) {
+  if constexpr (WL == 2) {
+    // nothing staged
+  } else if constexpr (WL == 1) {
     for (int64_t c = 8 * (int64_t)tid; c < H; c += 8 * NT) {
       float w[8];
       load_w8(w, p.gamma, c, p.w_dtype);
@@ -90,7 +93,20 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   }
   // the 8 weights of strip k (from LDS or registers)
   auto weights = [&](int k, float (&gk)[8], float (&bk)[8]) {
-    if constexpr (WL) {
+    if constexpr (WL == 2) {
+      const int64_t c = 8 * (int64_t)(tl + TEAM * k);
+      if (cv[k]) {
+        load_w8(gk, p.gamma, c, p.w_dtype);
+        if (p.zero_centered) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) gk[i] += 1.0f;
+        }
+        if constexpr (NORM == NT_LAYERNORM) load_w8(bk, p.beta, c, p.w_dtype);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gk[i] = bk[i] = 0.0f;
+      }
+    } else if constexpr (WL == 1) {
       const int c = 8 * (tl + TEAM * k);
       const float4 *s0 = reinterpret_cast<const float4 *>(wlds + c);
       float4 a = s0[0], d = s0[1];
@@ -132,14 +148,16 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   };
 
   // software pipeline: the next row's loads are issued before the current row is normalised
-  Strip<IN> cur[KC], nxt[KC];
+  // (not with WL == 2: the registers hold the weights in flight instead)
+  constexpr bool PF = WL != 2;
+  Strip<IN> cur[KC], nxt[PF ? KC : 1];
   int64_t base = (int64_t)blockIdx.x * T;
   load_row(cur, base + team);
   int iter = 0;
   for (; base < p.rows; base += stride, ++iter) {
     const int64_t row = base + team;
     const bool rv = row < p.rows;
-    load_row(nxt, base + stride + team);
+    if constexpr (PF) load_row(nxt, base + stride + team);
 
     // ---- lane-local statistics over its valid strips
     Stats st{0.0f, 0.0f, 0.0f};
@@ -156,6 +174,10 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
         }
       }
       const float m = n > 0.0f ? sm / n : 0.0f;
+      if constexpr (WL == 2) {  // reconvert below rather than keep 8 KC floats live
+#pragma unroll
+        for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
+      }
       float q = 0.0f;
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
@@ -197,6 +219,10 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
 
     const float mu = NORM == NT_LAYERNORM ? st.mean : 0.0f;
     const float rs = 1.0f / sqrtf(st.m2 * inv_h + p.eps);
+    if constexpr (WL == 2) {
+#pragma unroll
+      for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
+    }
     if (rv && tl == 0) {
       if (p.rsigma) p.rsigma[row] = rs;
       if constexpr (NORM == NT_LAYERNORM) {
@@ -204,7 +230,8 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
       }
     }
 
-    // ---- normalise and store
+    // ---- normalise and store (WL == 2: a scheduling barrier per strip keeps one strip's
+    // weights live at a time)
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       const bool ok = rv && cv[k];
@@ -227,7 +254,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
           if (ok) amax_local = fmaxf(amax_local, fabsf(y[i]));
         }
         const uint2 c = fp8_pack8(u, fmt);
-        if (ok) *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.y) + row * H + col) = c;
+        if (ok) st_nt8(static_cast<uint8_t *>(p.y) + row * H + col, c);
       } else {  // MODE_MX: 4 consecutive lanes hold one 32-element block
         float a = 0.0f;
 #pragma unroll
@@ -240,14 +267,19 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
         for (int i = 0; i < 8; ++i) u[i] = y[i] * f;
         const uint2 c = fp8_pack8(u, fmt);
         if (ok) {
-          *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.y) + row * H + col) = c;
+          st_nt8(static_cast<uint8_t *>(p.y) + row * H + col, c);
           if ((tl & 3) == 0)
             static_cast<uint8_t *>(p.scale_inv)[row * p.mx_cols + (col >> 5)] = (uint8_t)(X + 127);
         }
       }
+      if constexpr (WL == 2) __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (PF) {
 #pragma unroll
-    for (int k = 0; k < KC; ++k) cur[k] = nxt[k];
+      for (int k = 0; k < KC; ++k) cur[k] = nxt[k];
+    } else {
+      load_row(cur, base + stride + team);
+    }
   }
 
   if constexpr (MODE == MODE_DELAYED) {
@@ -278,9 +310,10 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
 // instantiation table
 // ------------------------------------------------------------------------------------------
 
-// weights go to LDS when the team's cover of float32 gamma (and beta) fits in 64 KB
+// weights go to LDS when the team's cover of float32 gamma (and beta) fits in 64 KB; with 8
+// strips per lane and a larger cover they are read per strip from the caches
 template <int NORM, int P, int KC> constexpr int wl_for() {
-  return (NORM == NT_LAYERNORM ? 2 : 1) * 8 * 64 * P * KC * 4 <= 65536 && KC >= 4 ? 1 : 0;
+  return (NORM == NT_LAYERNORM ? 2 : 1) * 8 * 64 * P * KC * 4 <= 65536 && KC >= 4 ? 1 : (KC >= 8 ? 2 : 0);
 }
 
 template <int NORM, class IN, int MODE>
@@ -297,6 +330,7 @@ static const void *pick_cfg(int cfg) {
     case ROW_W2T2_K4: return NF8_ROW(2, 2, 4);
     case ROW_W8_K1: return NF8_ROW(8, 1, 1);
     case ROW_W4T2_K2: return NF8_ROW(4, 2, 2);
+    case ROW_W16_K8: return NF8_ROW(16, 1, 8);
     default: return nullptr;
   }
 #undef NF8_ROW
