@@ -120,13 +120,14 @@ struct FwdPlan {
   int mode = MODE_PLAIN;
   bool rowwise = true, colwise = false;
   bool band = false;
-  bool col = false;  // band layout served by the 128-row columnwise kernel
-  int cfg = 0;
+  bool col = false;   // columnwise output in two passes: statistics (row kernel), then tiles
+  int cfg = 0;        // row layout (row path and the statistics pass) or band layout
   int tile_rows = 0;  // rows per band
   int S = 1;
   int64_t bands = 0;
   size_t ws_bytes = 0;
   size_t partial_off = 0;
+  size_t stats_off = 0;  // two-pass path: mu / rsigma when the caller passes none
 };
 
 int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
@@ -172,12 +173,14 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
         break;
       }
   }
-  pl->band = pl->colwise || row_cfg < 0 || force_band;
+  // a columnwise output goes through the statistics pass + tile kernel when a row layout covers
+  // the row (NORMFP8_COL_KERNEL=0 selects the single-pass band kernel instead)
+  pl->col = pl->colwise && row_cfg >= 0 && !force_band && env_int("NORMFP8_COL_KERNEL", 1) != 0;
+  pl->band = !pl->col && (pl->colwise || row_cfg < 0 || force_band);
   if (!pl->band) {
     pl->cfg = row_cfg;
   } else {
     int bc;
-    pl->col = pl->colwise && env_int("NORMFP8_COL_KERNEL", 1) != 0;
     if (pl->colwise) bc = hidden <= 512 ? BAND_R8_K1 : BAND_R8_K2;
     else bc = hidden <= 2048 ? BAND_R1_K4 : BAND_R2_K8;
     const int band_override = env_int("NORMFP8_BAND_CFG", -1);
@@ -186,8 +189,8 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
         !(pl->colwise && pl->mode == MODE_MX && kBandShapes[band_override].RW != 8))
       bc = band_override;
     pl->cfg = bc;
-    pl->tile_rows = pl->col ? kColTileRows : kBandShapes[bc].rows();
-    pl->S = (int)cdiv(hidden, pl->col ? kColTileCols : kBandShapes[bc].cols());
+    pl->tile_rows = kBandShapes[bc].rows();
+    pl->S = (int)cdiv(hidden, kBandShapes[bc].cols());
     pl->bands = cdiv(rows, pl->tile_rows);
     if (pl->S > kMaxSlices)
       return fail(NORM_ERR_UNSUPPORTED, "hidden %lld needs %d workgroups per band; this build allows %d",
@@ -201,6 +204,10 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     pl->partial_off = ws;
     const int nv = norm_type == NORM_LAYERNORM ? 2 : 1;
     ws += round_up((size_t)pl->bands * pl->S * pl->tile_rows * nv * sizeof(uint64_t), 256);
+  }
+  if (pl->col) {
+    pl->stats_off = ws;
+    ws += round_up((size_t)rows * sizeof(float) * (norm_type == NORM_LAYERNORM ? 2 : 1), 256);
   }
   pl->ws_bytes = ws;
   (void)in_dtype;
@@ -338,6 +345,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     // delayed scaling still publishes updated_amax = amax and scale_inv = 1/scale: one
     // workgroup of the row kernel does that without visiting any row
     pl.band = false;
+    pl.col = false;
     pl.cfg = ROW_W1_K1;
   }
 
@@ -366,19 +374,58 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   f.zero_centered = zero_centered_gamma ? 1 : 0;
   f.eps = epsilon;
 
-  if (!pl.band) {
-    const void *fn = fwd_row_kernel_ptr(norm_type, in_dtype, pl.mode, pl.cfg);
+  auto launch_rows = [&](const FwdRowParams &rp, int mode) -> int {
+    const void *fn = fwd_row_kernel_ptr(norm_type, in_dtype, mode, pl.cfg);
     if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no forward row kernel for this combination");
     const RowShape &sh = kRowShapes[pl.cfg];
     int occ = 1;
-    rc = occupancy(fn, sh.threads(), &occ);
-    if (rc) return rc;
+    int r = occupancy(fn, sh.threads(), &occ);
+    if (r) return r;
     int64_t grid = cdiv(rows, sh.T);
     int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
     if (cap > kMaxGrid) cap = kMaxGrid;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
-    rc = launch(fn, dim3((unsigned)grid), dim3(sh.threads()), &f, st);
+    FwdRowParams copy = rp;
+    return launch(fn, dim3((unsigned)grid), dim3(sh.threads()), &copy, st);
+  };
+  if (!pl.band && !pl.col) {
+    rc = launch_rows(f, pl.mode);
+    if (rc) return rc;
+    return ok();
+  }
+  if (pl.col) {
+    // pass 1: statistics of every row, into the caller's mu / rsigma or the workspace
+    float *st_mu = nullptr;
+    float *st_rs = rsigma ? rsigma : reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.stats_off);
+    if (ln) st_mu = mu ? mu : reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.stats_off) + rows;
+    FwdRowParams s = f;
+    s.y = nullptr;
+    s.mu = st_mu;
+    s.rsigma = st_rs;
+    rc = launch_rows(s, MODE_STATS);
+    if (rc) return rc;
+    // pass 2: independent 128 x 128 tiles
+    FwdTileParams tp{};
+    tp.f = f;
+    tp.y_col = y_colwise;
+    tp.col_scale_inv = colwise_scale_inv;
+    tp.st_mu = st_mu;
+    tp.st_rs = st_rs;
+    tp.mx_rows = cdiv(rows, 32);
+    tp.tiles_r = cdiv(rows, kColTileRows);
+    tp.tiles_c = cdiv(hidden, kColTileCols);
+    tp.write_row = pl.rowwise ? 1 : 0;
+    const void *fn = fwd_tile_kernel_ptr(norm_type, in_dtype, pl.mode);
+    if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no forward tile kernel for this combination");
+    int occ = 1;
+    rc = occupancy(fn, kColThreads, &occ);
+    if (rc) return rc;
+    int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
+    if (cap > kMaxGrid) cap = kMaxGrid;
+    const int64_t tiles = tp.tiles_r * tp.tiles_c;
+    const int64_t grid = tiles < cap ? tiles : cap;
+    rc = launch(fn, dim3((unsigned)grid), dim3(kColThreads), &tp, st);
     if (rc) return rc;
     return ok();
   }
@@ -392,10 +439,9 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   b.mx_rows = cdiv(rows, 32);
   b.S = pl.S;
   b.write_row = pl.rowwise ? 1 : 0;
-  const void *fn = pl.col ? fwd_col_kernel_ptr(norm_type, in_dtype, pl.mode)
-                          : fwd_band_kernel_ptr(norm_type, in_dtype, pl.mode, pl.colwise, pl.cfg);
+  const void *fn = fwd_band_kernel_ptr(norm_type, in_dtype, pl.mode, pl.colwise, pl.cfg);
   if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no forward band kernel for this combination");
-  const int threads = pl.col ? kColThreads : 256;
+  const int threads = 256;
   // persistent grid: at most what fits on the CUs left by the margin; the S workgroups of a
   // band wait for each other, so at least S must be able to run at once
   int occ = 1;

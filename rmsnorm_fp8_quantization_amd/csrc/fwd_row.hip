@@ -3,7 +3,8 @@
 // [XLA-Norm] = "Implementation: NVIDIA TransformerEngine JAX XLA Normalization".
 // [XLA-Norm] Overview / Description: LayerNorm or RMSNorm forward that writes the normalised
 // output (optionally FP8-quantised with delayed per-tensor or MXFP8 block scaling, in the
-// same kernel launch) plus mu (LayerNorm) and rsigma for the backward. [XLA-Norm] I/O Contract
+// same kernel launch) plus mu (LayerNorm) and rsigma for the backward. MODE_STATS writes only
+// mu / rsigma (the first pass of the columnwise path, see fwd_col.hip). [XLA-Norm] I/O Contract
 // lists the inputs (x, gamma, beta, scale, amax) and outputs (y, mu, rsigma, scale_inv,
 // updated amax) this kernel reads and writes.
 //
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   __shared__ float wlds[WL == 1 ? NW * COVER : 1];
   float g[WL ? 1 : KC][8];
   float b[(!WL && NORM == NT_LAYERNORM) ? KC : 1][8];
-  if constexpr (WL == 2) {
+  if constexpr (WL == 2 || MODE == MODE_STATS) {
     // nothing staged
   } else if constexpr (WL == 1) {
     for (int64_t c = 8 * (int64_t)tid; c < H; c += 8 * NT) {
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
     // ---- normalise and store (WL == 2: a scheduling barrier per strip keeps one strip's
     // weights live at a time)
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
+    for (int k = 0; k < (MODE == MODE_STATS ? 0 : KC); ++k) {
       const bool ok = rv && cv[k];
       const int64_t col = 8 * (int64_t)(tl + TEAM * k);
       float gk[8], bk[8], xv[8], y[8];
@@ -342,6 +343,7 @@ static const void *pick_mode(int mode, int cfg) {
     case MODE_PLAIN: return pick_cfg<NORM, IN, MODE_PLAIN>(cfg);
     case MODE_DELAYED: return pick_cfg<NORM, IN, MODE_DELAYED>(cfg);
     case MODE_MX: return pick_cfg<NORM, IN, MODE_MX>(cfg);
+    case MODE_STATS: return pick_cfg<NORM, IN, MODE_STATS>(cfg);
     default: return nullptr;
   }
 }

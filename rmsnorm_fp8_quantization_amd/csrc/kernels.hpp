@@ -58,14 +58,14 @@ struct BwdShape {
 };
 constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1}, {4, 1}, {4, 2}, {8, 2}, {16, 2}, {8, 1}, {16, 1}, {4, 4}};
 
-// ---- forward columnwise kernel: 16 waves, tiles of 128 rows x 512 columns
+// ---- forward tile kernel (second pass of a columnwise output): 4 waves, 128 x 128 tiles
 constexpr int kColTileRows = 128;
-constexpr int kColTileCols = 512;
-constexpr int kColThreads = 1024;
+constexpr int kColTileCols = 128;
+constexpr int kColThreads = 256;
 
 const void *fwd_row_kernel_ptr(int norm, int in_dtype, int mode, int cfg);
 const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg);
-const void *fwd_col_kernel_ptr(int norm, int in_dtype, int mode);
+const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode);
 const void *bwd_kernel_ptr(int norm, int in_dtype, bool add, int cfg);
 const void *bwd_finalize_kernel_ptr();
 const void *ws_init_kernel_ptr();

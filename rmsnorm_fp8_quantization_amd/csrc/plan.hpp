@@ -16,8 +16,8 @@ namespace nf8 {
 // element-type codes (identical to norm_dtype_t)
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
 enum : int { NT_LAYERNORM = 0, NT_RMSNORM = 1 };
-// epilogue modes
-enum : int { MODE_PLAIN = 0, MODE_DELAYED = 1, MODE_MX = 2 };
+// epilogue modes (MODE_STATS: statistics only, written to mu / rsigma; no output)
+enum : int { MODE_PLAIN = 0, MODE_DELAYED = 1, MODE_MX = 2, MODE_STATS = 3 };
 
 // time limit of a cross-workgroup wait, in ticks of the 100 MHz real-time counter (2 s)
 constexpr uint64_t kSpinLimitTicks = 200000000ull;
@@ -86,6 +86,21 @@ struct FwdBandParams {
   int64_t mx_rows;       // ceil(rows / 32)
   int S;                 // workgroups per band
   int classes;           // ticket classes (1 or kClasses); gridDim.x is a multiple of it
+  int write_row;         // rowwise output requested
+};
+
+// ---- forward tile kernel (second pass of a columnwise output) -------------------------------
+// Independent tiles of 128 rows x 128 columns, each normalised with the row statistics the
+// first pass (row kernel, MODE_STATS) wrote to st_mu / st_rs.
+struct FwdTileParams {
+  FwdRowParams f;        // shared fields (y = rowwise output or nullptr)
+  void *y_col;           // [hidden, rows] columnwise codes
+  void *col_scale_inv;   // delayed: float32[1]; MX: uint8 [hidden, ceil(rows/32)]
+  const float *st_mu;    // [rows] (LayerNorm)
+  const float *st_rs;    // [rows]
+  int64_t mx_rows;       // ceil(rows / 32)
+  int64_t tiles_r;       // ceil(rows / 128)
+  int64_t tiles_c;       // ceil(hidden / 128)
   int write_row;         // rowwise output requested
 };
 

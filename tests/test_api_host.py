@@ -76,11 +76,11 @@ def test_fwd_workspace_queries():
     assert rc == L.NORM_OK and n > L.NORM_WS_HEADER_BYTES             # header + band partials
     rc, n2 = fwd_ws(32768, 8192, out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_DELAYED_TENSOR)
     assert rc == L.NORM_OK and n2 == L.NORM_WS_HEADER_BYTES           # amax needs the header only
-    rc, n3 = fwd_ws(1024, 65536, norm=L.NORM_LAYERNORM)               # long rows: split path
+    rc, n3 = fwd_ws(1024, 131072, norm=L.NORM_LAYERNORM)              # beyond the row layouts: split path
     assert rc == L.NORM_OK and n3 > L.NORM_WS_HEADER_BYTES
     # deterministic and monotone in rows
-    assert fwd_ws(1024, 65536, norm=L.NORM_LAYERNORM) == (rc, n3)
-    assert fwd_ws(2048, 65536, norm=L.NORM_LAYERNORM)[1] >= n3
+    assert fwd_ws(1024, 131072, norm=L.NORM_LAYERNORM) == (rc, n3)
+    assert fwd_ws(2048, 131072, norm=L.NORM_LAYERNORM)[1] >= n3
     # rows == 0 is valid
     assert fwd_ws(0, 4096)[0] == L.NORM_OK
 
