@@ -53,24 +53,42 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
   __shared__ float red[2][W][2];
   const float inv_h = 1.0f / (float)H;
 
-  int iter = 0;
-  for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x, ++iter) {
+  // The next row's dy, x (and residual) are loaded while the current row is processed. The
+  // loads are unconditional (a row past the end reads row 0, a strip past the end of the row
+  // reads column 0) and masked where they are used: under a branch a load may not have been
+  // issued, and the wait before the current row's first use would then drain the prefetch too.
+  struct RowData {
     Strip<IN> dys[KC], xs[KC], rsd[ADD ? KC : 1];
+    float rs, mu;
+  };
+  auto load_row = [&](RowData &d, int64_t row) {
+    const int64_t r = row < p.rows ? row : 0;
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      const int64_t off = row * H + 8 * (int64_t)(tid + NT * k);
-      if (cv[k]) {
-        load_strip<IN>(dys[k], p.dy, off);
-        load_strip<IN>(xs[k], p.x, off);
-        if constexpr (ADD) load_strip<IN>(rsd[k], p.residual, off);
-      } else {
-        zero_strip<IN>(dys[k]);
-        zero_strip<IN>(xs[k]);
-        if constexpr (ADD) zero_strip<IN>(rsd[k]);
+      const int64_t off = r * H + (cv[k] ? 8 * (int64_t)(tid + NT * k) : 0);
+      load_strip<IN>(d.dys[k], p.dy, off);
+      load_strip<IN>(d.xs[k], p.x, off);
+      if constexpr (ADD) load_strip<IN>(d.rsd[k], p.residual, off);
+    }
+    d.rs = p.rsigma[r];
+    d.mu = NORM == NT_LAYERNORM ? p.mu[r] : 0.0f;
+  };
+
+  // one row: statistics, dx, and the weight-gradient partial sums
+  auto step = [&](RowData &cur, int64_t row, int iter) {
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      if (!cv[k]) {
+        zero_strip<IN>(cur.dys[k]);
+        zero_strip<IN>(cur.xs[k]);
+        if constexpr (ADD) zero_strip<IN>(cur.rsd[k]);
       }
     }
-    const float rs = p.rsigma[row];
-    const float mu = NORM == NT_LAYERNORM ? p.mu[row] : 0.0f;
+    const Strip<IN> *const dys = cur.dys;
+    const Strip<IN> *const xs = cur.xs;
+    const Strip<IN> *const rsd = cur.rsd;
+    const float rs = cur.rs;
+    const float mu = cur.mu;
 
     // row sums of w = dy * g and w * xhat
     float s1 = 0.0f, s2 = 0.0f;
@@ -125,6 +143,23 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
       }
       if (cv[k]) store_t8<IN>(p.dx, row * H + 8 * (int64_t)(tid + NT * k), out);
     }
+  };
+
+  // Two row buffers used in turn, so that the next row's loads never wait on the current
+  // row's registers. (Not for 16 waves x 2 strips: two rows of inputs would not fit the
+  // register budget; those load each row after the previous one is done.)
+  constexpr bool PF = !(W == 16 && KC >= 2);
+  const int64_t G = gridDim.x;
+  RowData a, b;
+  load_row(a, blockIdx.x);
+  for (int64_t row = blockIdx.x, iter = 0; row < p.rows; row += 2 * G, iter += 2) {
+    if constexpr (PF) load_row(b, row + G);
+    step(a, row, (int)iter);
+    if (row + G >= p.rows) break;
+    if constexpr (PF) load_row(a, row + 2 * G);
+    else load_row(b, row + G);
+    step(b, row + G, (int)iter + 1);
+    if constexpr (!PF) load_row(a, row + 2 * G);
   }
 
   // this workgroup's partial weight gradients

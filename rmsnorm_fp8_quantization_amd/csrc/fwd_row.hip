@@ -34,6 +34,9 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   constexpr int NT = TEAM * T;
   constexpr int COVER = 8 * TEAM * KC;                      // row elements one team holds
   constexpr int NW = NORM == NT_LAYERNORM ? 2 : 1;          // weight arrays
+  // many strips per lane: convert them again for each pass instead of keeping 8 KC floats
+  // live, which would leave no room for the next row's loads
+  constexpr bool RECONV = WL == 2 || KC >= 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -140,12 +143,14 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   const float inv_h = 1.0f / (float)H;
   const int64_t stride = (int64_t)gridDim.x * T;
 
+  // Loads are unconditional (rows past the end read row 0, strips past the end of the row read
+  // column 0) and the strips are masked where they are used: a load under a branch may not have
+  // been issued, so the wait before the current row's first use would have to drain the
+  // prefetch of the next row as well.
   auto load_row = [&](Strip<IN> (&xs)[KC], int64_t row) {
+    const int64_t r = row < p.rows ? row : 0;
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      if (row < p.rows && cv[k]) load_strip<IN>(xs[k], p.x, row * H + 8 * (int64_t)(tl + TEAM * k));
-      else zero_strip<IN>(xs[k]);
-    }
+    for (int k = 0; k < KC; ++k) load_strip<IN>(xs[k], p.x, r * H + (cv[k] ? 8 * (int64_t)(tl + TEAM * k) : 0));
   };
 
   // software pipeline: the next row's loads are issued before the current row is normalised
@@ -159,6 +164,9 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
     const int64_t row = base + team;
     const bool rv = row < p.rows;
     if constexpr (PF) load_row(nxt, base + stride + team);
+#pragma unroll
+    for (int k = 0; k < KC; ++k)
+      if (!(rv && cv[k])) zero_strip<IN>(cur[k]);
 
     // ---- lane-local statistics over its valid strips
     Stats st{0.0f, 0.0f, 0.0f};
@@ -175,7 +183,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
         }
       }
       const float m = n > 0.0f ? sm / n : 0.0f;
-      if constexpr (WL == 2) {  // reconvert below rather than keep 8 KC floats live
+      if constexpr (RECONV) {
 #pragma unroll
         for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
       }
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
 
     const float mu = NORM == NT_LAYERNORM ? st.mean : 0.0f;
     const float rs = 1.0f / sqrtf(st.m2 * inv_h + p.eps);
-    if constexpr (WL == 2) {
+    if constexpr (RECONV) {
 #pragma unroll
       for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
     }
