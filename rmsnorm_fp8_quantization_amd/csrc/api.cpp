@@ -175,7 +175,10 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   }
   // a columnwise output goes through the statistics pass + tile kernel when a row layout covers
   // the row (NORMFP8_COL_KERNEL=0 selects the single-pass band kernel instead)
-  pl->col = pl->colwise && row_cfg >= 0 && !force_band && env_int("NORMFP8_COL_KERNEL", 1) != 0;
+  // (the tile kernel's lane offsets are 32-bit: 128 rows of float32 input, 128 columns of the
+  // transposed output)
+  const bool tile_fits = (int64_t)hidden * 4 * kColTileRows < (1ll << 32) && rows * kColTileCols < (1ll << 32);
+  pl->col = pl->colwise && row_cfg >= 0 && tile_fits && !force_band && env_int("NORMFP8_COL_KERNEL", 1) != 0;
   pl->band = !pl->col && (pl->colwise || row_cfg < 0 || force_band);
   if (!pl->band) {
     pl->cfg = row_cfg;

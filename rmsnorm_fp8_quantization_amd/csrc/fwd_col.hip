@@ -11,17 +11,20 @@
 // Two passes: the row kernel first writes mu / rsigma of every row (MODE_STATS); this kernel
 // then works on independent tiles. A column of the transposed output is contiguous along
 // rows and column pieces shorter than a 128-byte line are not merged on their way to HBM, so
-// a tile spans 128 rows; with statistics known in advance no tile waits for another one,
-// which keeps many small workgroups resident per CU. The price is a second read of x.
+// a tile spans 128 rows; with statistics known in advance no tile waits for another one. The
+// price is a second read of x; tiles are visited from the last row down, so the first ones
+// read rows the statistics pass streamed most recently (still in the last-level cache).
 //
-// Work split: a workgroup of 4 waves owns a tile of 128 rows x 128 columns; wave w owns rows
-// [32w, 32w + 32); lane l holds rows 32w + 8 (l >> 4) + k (k < 8) of the 8 columns
+// Work split: a workgroup of 8 waves owns a tile of 128 rows x 128 columns; wave w owns rows
+// [16w, 16w + 16); lane l holds rows 16w + 4 (l >> 4) + k (k < 4) of the 8 columns
 // 8 (l % 16) + 0..7, so one load instruction covers 4 rows x 256 bytes and one rowwise store
-// 4 whole 128-byte lines. FP8 codes of a lane's 8 x 8 block are transposed in registers (4 x 4
-// byte blocks) into its 8 columns' 8-row pieces, staged in LDS as [column][128 rows] with the
-// pieces XOR-swizzled across banks, and stored so that 8 consecutive lanes write a column's
-// 128-byte line. An MXFP8 columnwise block (32 rows) is one wave: its per-column maxima
-// combine across the wave's four 16-lane row groups.
+// 4 whole 128-byte lines. The next tile's inputs are loaded while the current tile is
+// processed (two register buffers used in turn). FP8 codes of a lane's 4 x 8 block are
+// transposed in registers (4 x 4 byte blocks) into its 8 columns' 4-row pieces, staged in LDS
+// (two buffers, used in turn) as [column][128 rows] with 16-byte groups XOR-swizzled across
+// banks, and stored so that 8 consecutive lanes write a column's 128-byte line. An MXFP8
+// columnwise block (32 rows) is two waves: each wave reduces its 16 rows per column and the
+// pair combine through LDS.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -46,9 +49,10 @@ __device__ __forceinline__ void transpose4x4b(uint32_t a0, uint32_t a1, uint32_t
   o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
-// byte offset in the staging buffer of rows [8 piece, 8 piece + 8) of tile column `col`
+// byte offset in a staging buffer of rows [4 piece, 4 piece + 4) of tile column `col`: the
+// column's 128 bytes, with its eight 16-byte groups permuted by XOR with (col / 8) % 8
 __device__ __forceinline__ int stage_off(int col, int piece) {
-  return col * kTR + 8 * (piece ^ ((col >> 3) & 15));
+  return col * kTR + 4 * (piece ^ (((col >> 3) & 7) << 2));
 }
 
 // max over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the same columns in the four row groups)
@@ -57,79 +61,112 @@ __device__ __forceinline__ float rowgroup_max(float v) {
   return fmaxf(v, xor32(v));
 }
 
-// 8 consecutive floats of a per-row array starting at row r (rows >= n read as 0)
-__device__ __forceinline__ void load_rows8(float (&o)[8], const float *a, int64_t r, int64_t n) {
-  if (r + 8 <= n) {
-    const float4 u = *reinterpret_cast<const float4 *>(a + r);
-    const float4 v = *reinterpret_cast<const float4 *>(a + r + 4);
-    o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w; o[4] = v.x; o[5] = v.y; o[6] = v.z; o[7] = v.w;
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) o[k] = r + k < n ? a[r + k] : 0.0f;
-  }
-}
-
 }  // namespace
 
 template <int NORM, class IN, int MODE>
-__global__ __launch_bounds__(256) void fwd_tile_kernel(FwdTileParams tp) {
+__global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp) {
   static_assert(MODE == MODE_DELAYED || MODE == MODE_MX, "columnwise output is FP8");
+  static_assert(kColThreads == 512, "8 waves of 16 rows");
   const FwdRowParams &p = tp.f;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rg = lane >> 4;  // row group: rows 8 rg .. 8 rg + 7 of the wave
+  const int rg = lane >> 4;  // row group: rows 4 rg .. 4 rg + 3 of the wave
   const int cl = lane & 15;  // columns 8 cl .. 8 cl + 7 of the tile
   const int64_t H = p.hidden;
   const int64_t N = p.rows;
   const int fmt = p.out_dtype;
+  const uint32_t tiles_c = (uint32_t)tp.tiles_c;
+  const uint32_t ntiles = (uint32_t)(tp.tiles_r * tp.tiles_c);
+  // lane offsets within a tile are 32-bit (the planner bounds 128 * hidden * 4 and
+  // 128 * rows below 2^32); tile bases are wave-uniform 64-bit pointers
+  const uint32_t Hu = (uint32_t)H;
+  const uint32_t Nu = (uint32_t)N;
+  const int rloc = 16 * wave + 4 * rg;  // this lane's first row within a tile
+  const int cloc = 8 * cl;              // this lane's first column within a tile
 
-  __shared__ __align__(16) uint8_t stage[kTC * kTR];
+  __shared__ __align__(16) uint8_t stage[2][kTC * kTR];
+  __shared__ __align__(16) float cmax[MODE == MODE_MX ? 8 : 1][MODE == MODE_MX ? kTC : 4];
   __shared__ uint8_t colx[MODE == MODE_MX ? 4 : 1][MODE == MODE_MX ? kTC : 1];
   __shared__ uint32_t s_last, s_epoch;
-  __shared__ float wred[4];
+  __shared__ float wred[kColThreads / 64];
 
   const uint32_t tag = MODE == MODE_DELAYED ? epoch_tag(read_epoch(p.ws, &s_epoch)) : 0u;
   float scale = 1.0f;
   if constexpr (MODE == MODE_DELAYED) scale = *p.scale;
   float amax_local = 0.0f;
 
-  const int64_t ntiles = tp.tiles_r * tp.tiles_c;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t rt = t / tp.tiles_c;
-    const int64_t ct = t - rt * tp.tiles_c;
-    const int64_t r0 = rt * kTR;                   // first row of the tile
-    const int64_t c0 = ct * kTC;                   // first column of the tile
-    const int64_t rl = r0 + 32 * wave + 8 * rg;    // first row of this lane
-    const int64_t col = c0 + 8 * cl;               // first column of this lane
-    const bool cv = col < H;
-    const int valid = (int)(N - rl < 8 ? (N - rl < 0 ? 0 : N - rl) : 8);  // this lane's rows
+  // tile t covers rows [128 rt, +128) and columns [128 ct, +128), visited from the last tile
+  struct Tile {
+    uint32_t rt, ct;
+    int64_t r0, c0;
+    int rows_here, cols_here;  // valid rows / columns of the tile (up to 128)
+  };
+  auto tile_of = [&](uint32_t t) {
+    Tile T;
+    const uint32_t u = ntiles - 1u - t;
+    T.rt = u / tiles_c;
+    T.ct = u - T.rt * tiles_c;
+    T.r0 = (int64_t)T.rt * kTR;
+    T.c0 = (int64_t)T.ct * kTC;
+    T.rows_here = (int)(N - T.r0 < kTR ? N - T.r0 : kTR);
+    T.cols_here = (int)(H - T.c0 < kTC ? H - T.c0 : kTC);
+    return T;
+  };
 
-    // ---- inputs
-    Strip<IN> xs[8];
+  // This lane's 4 x 8 inputs of tile t. The loads are unconditional (t past the end reads
+  // tile 0, rows and columns past the end of a tile read its first row / column) so that no
+  // branch makes the number of loads in flight uncertain; what lies outside the tensor is
+  // never stored.
+  struct TileIn {
+    Strip<IN> xs[4];
+  };
+  auto load_tile = [&](TileIn &d, uint32_t t) {
+    const Tile T = tile_of(t < ntiles ? t : 0u);
+    const char *xb = static_cast<const char *>(p.x) + (T.r0 * H + T.c0) * IN::bytes;
+    const uint32_t co = cloc < T.cols_here ? (uint32_t)cloc : 0u;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k < valid && cv) load_strip<IN>(xs[k], p.x, (rl + k) * H + col);
-      else zero_strip<IN>(xs[k]);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t r = rloc + k < T.rows_here ? (uint32_t)(rloc + k) : 0u;
+      load_strip<IN>(d.xs[k], xb + (size_t)((r * Hu + co) * (uint32_t)IN::bytes), 0);
     }
-    float rs[8], mu[8];
-    load_rows8(rs, tp.st_rs, rl, N);
-    if constexpr (NORM == NT_LAYERNORM) load_rows8(mu, tp.st_mu, rl, N);
+  };
+
+  auto step = [&](TileIn &cur, uint32_t t, TileIn &nxt, uint32_t tn, int par) {
+    const Tile T = tile_of(t);
+    const bool cv = cloc < T.cols_here;
+    const int valid = T.rows_here - rloc < 4 ? (T.rows_here - rloc < 0 ? 0 : T.rows_here - rloc) : 4;
+    uint8_t *const stg = stage[par];
+
+    // ---- weights and row statistics of this tile, then the next tile's inputs
     float gk[8], bk[8];
     if (cv) {
-      load_w8(gk, p.gamma, col, p.w_dtype);
+      load_w8(gk, p.gamma, T.c0 + cloc, p.w_dtype);
       if (p.zero_centered) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) gk[i] += 1.0f;
       }
-      if constexpr (NORM == NT_LAYERNORM) load_w8(bk, p.beta, col, p.w_dtype);
+      if constexpr (NORM == NT_LAYERNORM) load_w8(bk, p.beta, T.c0 + cloc, p.w_dtype);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) gk[i] = bk[i] = 0.0f;
     }
+    float rs[4], mu[4];
+    {
+      const float *rsb = tp.st_rs + T.r0;
+      const float *mub = tp.st_mu + T.r0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t r = rloc + k < T.rows_here ? (uint32_t)(rloc + k) : 0u;
+        rs[k] = rsb[r];
+        if constexpr (NORM == NT_LAYERNORM) mu[k] = mub[r];
+      }
+    }
+    load_tile(nxt, tn);
+
     auto yrow = [&](int k, float (&y)[8]) {
       float xv[8];
-      strip_to_f32<IN>(xs[k], xv);
+      strip_to_f32<IN>(cur.xs[k], xv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if constexpr (NORM == NT_LAYERNORM) y[i] = fmaf((xv[i] - mu[k]) * rs[k], gk[i], bk[i]);
@@ -137,14 +174,14 @@ __global__ __launch_bounds__(256) void fwd_tile_kernel(FwdTileParams tp) {
       }
     };
 
-    // ---- MXFP8 columnwise scales: the 32-row block is this wave. For RMSNorm
+    // ---- MXFP8 columnwise scales: a 32-row block is waves 2b, 2b + 1. For RMSNorm
     // max_r |(x_r rs_r) g| = max_r |x_r rs_r| * |g| exactly (binary32 rounding is monotone), so
     // g is applied once per column.
     float colf[8];
     if constexpr (MODE == MODE_MX) {
       float cm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 4; ++k) {
         if (k < valid) {
           if constexpr (NORM == NT_LAYERNORM) {
             float y[8];
@@ -153,112 +190,134 @@ __global__ __launch_bounds__(256) void fwd_tile_kernel(FwdTileParams tp) {
             for (int i = 0; i < 8; ++i) cm[i] = fmaxf(cm[i], fabsf(y[i]));
           } else {
             float xv[8];
-            strip_to_f32<IN>(xs[k], xv);
+            strip_to_f32<IN>(cur.xs[k], xv);
 #pragma unroll
             for (int i = 0; i < 8; ++i) cm[i] = fmaxf(cm[i], fabsf(xv[i] * rs[k]));
           }
         }
       }
+      // converted again below rather than kept live as floats
+#pragma unroll
+      for (int k = 0; k < 4; ++k) opaque<IN>(cur.xs[k]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cm[i] = rowgroup_max(cm[i]);
+      if (rg == 0) {
+        float4 *d = reinterpret_cast<float4 *>(&cmax[wave][cloc]);
+        d[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+        d[1] = make_float4(cm[4], cm[5], cm[6], cm[7]);
+      }
+      __syncthreads();
+      const float4 *o = reinterpret_cast<const float4 *>(&cmax[wave ^ 1][cloc]);
+      const float4 o0 = o[0], o1 = o[1];
+      const float om[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float a = rowgroup_max(cm[i]);
+        float a = fmaxf(cm[i], om[i]);
         if constexpr (NORM != NT_LAYERNORM) a = a * fabsf(gk[i]);
         const int X = mx_exponent(a, fmt);
         colf[i] = exp2_neg(X);
-        if (rg == 0) colx[wave][8 * cl + i] = (uint8_t)(X + 127);
+        if (rg == 0 && (wave & 1) == 0) colx[wave >> 1][cloc + i] = (uint8_t)(X + 127);
       }
     }
 
     // ---- codes: rowwise stores; columnwise codes transposed into the staging buffer
+    uint8_t *const yb = static_cast<uint8_t *>(p.y) + T.r0 * H + T.c0;
+    uint8_t *const sb = MODE == MODE_MX ? static_cast<uint8_t *>(p.scale_inv) + T.r0 * p.mx_cols + (T.c0 >> 5)
+                                        : nullptr;
+    uint2 codes[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint2 codes[4];
+    for (int k = 0; k < 4; ++k) {
+      const bool ok = k < valid && cv;
+      uint8_t *const yr = yb + (size_t)((uint32_t)(rloc + k) * Hu + (uint32_t)cloc);
+      float y[8];
+      yrow(k, y);
+      if constexpr (MODE == MODE_DELAYED) {
+        float u[8];
+        float a = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int k = 4 * h + kk;
-        const bool ok = k < valid && cv;
-        uint8_t *const yr = static_cast<uint8_t *>(p.y) + (rl + k) * H + col;
-        float y[8];
-        yrow(k, y);
-        if constexpr (MODE == MODE_DELAYED) {
-          float u[8];
+        for (int i = 0; i < 8; ++i) {
+          u[i] = y[i] * scale;
+          a = fmaxf(a, fabsf(y[i]));
+        }
+        if (ok) amax_local = fmaxf(amax_local, a);
+        codes[k] = fp8_pack8(u, fmt);
+        if (ok && tp.write_row) st_nt8(yr, codes[k]);
+      } else {
+        if (tp.write_row) {
           float a = 0.0f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            u[i] = y[i] * scale;
-            a = fmaxf(a, fabsf(y[i]));
-          }
-          if (ok) amax_local = fmaxf(amax_local, a);
-          codes[kk] = fp8_pack8(u, fmt);
-          if (ok && tp.write_row) st_nt8(yr, codes[kk]);
-        } else {
-          if (tp.write_row) {
-            float a = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[i]));
-            a = quad_max(ok ? a : 0.0f);  // 4 lanes = one 32-column block
-            const int X = mx_exponent(a, fmt);
-            const float f = exp2_neg(X);
-            float u[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) u[i] = y[i] * f;
-            const uint2 c = fp8_pack8(u, fmt);
-            if (ok) {
-              st_nt8(yr, c);
-              if ((cl & 3) == 0)
-                static_cast<uint8_t *>(p.scale_inv)[(rl + k) * p.mx_cols + (col >> 5)] = (uint8_t)(X + 127);
-            }
-          }
+          for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[i]));
+          a = quad_max(ok ? a : 0.0f);  // 4 lanes = one 32-column block
+          const int X = mx_exponent(a, fmt);
+          const float f = exp2_neg(X);
           float u[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) u[i] = y[i] * colf[i];
-          codes[kk] = fp8_pack8(u, fmt);
+          for (int i = 0; i < 8; ++i) u[i] = y[i] * f;
+          const uint2 c = fp8_pack8(u, fmt);
+          if (ok) {
+            st_nt8(yr, c);
+            if ((cl & 3) == 0)
+              sb[(size_t)((uint32_t)(rloc + k) * (uint32_t)p.mx_cols + (uint32_t)(cloc >> 5))] = (uint8_t)(X + 127);
+          }
         }
+        float u[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[i] = y[i] * colf[i];
+        codes[k] = fp8_pack8(u, fmt);
       }
-      uint32_t lo[4], hi[4];  // lo[i]: column i, hi[i]: column 4 + i; byte kk = row 4h + kk
+    }
+    {
+      uint32_t lo[4], hi[4];  // lo[i]: column i, hi[i]: column 4 + i; byte k = row k
       transpose4x4b(codes[0].x, codes[1].x, codes[2].x, codes[3].x, lo);
       transpose4x4b(codes[0].y, codes[1].y, codes[2].y, codes[3].y, hi);
-      const int piece = 4 * wave + rg;  // rows 8 piece .. 8 piece + 7 of the tile
+      const int piece = 4 * wave + rg;  // rows 4 piece .. 4 piece + 3 of the tile
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<uint32_t *>(stage + stage_off(8 * cl + i, piece) + 4 * h) = i < 4 ? lo[i] : hi[i - 4];
+        *reinterpret_cast<uint32_t *>(stg + stage_off(cloc + i, piece)) = i < 4 ? lo[i] : hi[i - 4];
     }
     __syncthreads();
 
     // ---- columnwise stores: thread (c, m) writes rows [16m, 16m + 16) of tile column c
-    {
-      const int64_t rows_here = N - r0;  // valid rows of this tile (may be < 128)
-      const bool full = rows_here >= kTR && (N % 16) == 0;
-      uint8_t *const yct = static_cast<uint8_t *>(tp.y_col) + c0 * N + r0;
-      const int m = tid & 7;
+    const bool full = T.rows_here == kTR && (N % 16) == 0;
+    uint8_t *const yct = static_cast<uint8_t *>(tp.y_col) + T.c0 * N + T.r0;
+    const int m = tid & 7;
 #pragma unroll
-      for (int pass = 0; pass < kTC / 32; ++pass) {
-        const int c = pass * 32 + (tid >> 3);
-        if (c0 + c < H) {
-          const int slot = (2 * m) ^ ((c >> 3) & 15);  // piece 2m; piece 2m + 1 is at slot ^ 1
-          const uint2 a = *reinterpret_cast<const uint2 *>(stage + c * kTR + 8 * slot);
-          const uint2 b = *reinterpret_cast<const uint2 *>(stage + c * kTR + 8 * (slot ^ 1));
-          uint8_t *dst = yct + (int64_t)c * N + 16 * m;
-          if (full) {
-            st_nt16(dst, make_uint4(a.x, a.y, b.x, b.y));
-          } else {
-            const uint32_t w[4] = {a.x, a.y, b.x, b.y};
+    for (int pass = 0; pass < kTC / 64; ++pass) {
+      const int c = pass * 64 + (tid >> 3);
+      if (c < T.cols_here) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(stg + stage_off(c, 4 * m));
+        uint8_t *dst = yct + (size_t)((uint32_t)c * Nu + (uint32_t)(16 * m));
+        if (full) {
+          st_nt16(dst, v);
+        } else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (16 * m + e < rows_here) dst[e] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
-          }
-        }
-      }
-      if constexpr (MODE == MODE_MX) {
-        // the tile's (up to) four 32-row block exponents of each column, consecutive bytes
-        if (tid < kTC && c0 + tid < H) {
-          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + (c0 + tid) * tp.mx_rows + 4 * rt;
-          const int64_t nb = (rows_here + 31) / 32;
-          for (int q = 0; q < 4 && q < nb; ++q) dst[q] = colx[q][tid];
+          for (int e = 0; e < 16; ++e)
+            if (16 * m + e < T.rows_here) dst[e] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
         }
       }
     }
-    __syncthreads();  // the staging buffer and colx are rewritten by the next tile
+    if constexpr (MODE == MODE_MX) {
+      // the tile's (up to) four 32-row block exponents of each column, consecutive bytes
+      if (tid < T.cols_here) {
+        uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + T.c0 * tp.mx_rows + 4 * (int64_t)T.rt +
+                       (size_t)((uint32_t)tid * (uint32_t)tp.mx_rows);
+        const int nb = (T.rows_here + 31) / 32;
+        for (int q = 0; q < nb; ++q) dst[q] = colx[q][tid];
+      }
+    }
+    // No barrier here: the next tile stages into the other buffer, and it rewrites cmax /
+    // colx only after its first barrier, which every thread reaches after finishing this tile.
+  };
+
+  // two input buffers in turn: tile t is processed while tile t + G loads
+  const uint32_t G = gridDim.x;
+  TileIn A, B;
+  load_tile(A, blockIdx.x);
+  for (uint32_t t = blockIdx.x; t < ntiles; t += 2 * G) {
+    step(A, t, B, t + G, 0);
+    if (t + G >= ntiles) break;
+    step(B, t + G, A, t + 2 * G, 1);
   }
 
   // ---- delayed scaling: tensor amax through the per-workgroup tagged slots
@@ -267,7 +326,9 @@ __global__ __launch_bounds__(256) void fwd_tile_kernel(FwdTileParams tp) {
     if (lane == 0) wred[wave] = m;
     __syncthreads();
     if (tid == 0) {
-      publish_amax(p.ws, fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3])), tag);
+      float a = wred[0];
+      for (int w = 1; w < kColThreads / 64; ++w) a = fmaxf(a, wred[w]);
+      publish_amax(p.ws, a, tag);
       if (blockIdx.x == 0) {
         if (p.scale_inv) *static_cast<float *>(p.scale_inv) = 1.0f / scale;
         if (tp.col_scale_inv) *static_cast<float *>(tp.col_scale_inv) = 1.0f / scale;

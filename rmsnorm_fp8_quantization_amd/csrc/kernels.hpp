@@ -58,10 +58,10 @@ struct BwdShape {
 };
 constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1}, {4, 1}, {4, 2}, {8, 2}, {16, 2}, {8, 1}, {16, 1}, {4, 4}};
 
-// ---- forward tile kernel (second pass of a columnwise output): 4 waves, 128 x 128 tiles
+// ---- forward tile kernel (second pass of a columnwise output): 8 waves, 128 x 128 tiles
 constexpr int kColTileRows = 128;
 constexpr int kColTileCols = 128;
-constexpr int kColThreads = 256;
+constexpr int kColThreads = 512;
 
 const void *fwd_row_kernel_ptr(int norm, int in_dtype, int mode, int cfg);
 const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg);
