@@ -101,8 +101,9 @@ int norm_bwd_workspace_size(int64_t rows, int64_t hidden, int in_dtype, int w_dt
 
 /*
  * norm_fwd -- normalise each row of x and store the output, optionally FP8-quantised, in one
- * kernel launch. [XLA-Norm] Overview, Description, Signature (NormForwardFFI argument list),
- * I/O Contract.
+ * kernel launch (two when a columnwise layout is requested: the row statistics first, then the
+ * codes; both on `stream`). [XLA-Norm] Overview, Description, Signature (NormForwardFFI
+ * argument list), I/O Contract.
  *
  *   x [rows, hidden] in_dtype; gamma [hidden] w_dtype; beta [hidden] w_dtype (LayerNorm only,
  *   must be NULL for RMSNorm).

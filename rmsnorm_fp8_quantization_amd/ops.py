@@ -145,7 +145,8 @@ def prepare_fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tenso
 
 def fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor] = None,
         **kw) -> Dict[str, torch.Tensor]:
-    """LayerNorm / RMSNorm forward with an optional FP8 epilogue, in one kernel launch.
+    """LayerNorm / RMSNorm forward with an optional FP8 epilogue (one kernel launch; two for a
+    columnwise output: row statistics, then 128 x 128 tiles).
 
     x: [rows, hidden] (f32/f16/bf16); gamma, beta: [hidden]. Keywords: norm ("layernorm" |
     "rmsnorm"), eps, zero_centered_gamma, scaling ("none" | "delayed" | "mxfp8"), out_dtype
