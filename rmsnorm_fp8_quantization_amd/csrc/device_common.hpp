@@ -104,6 +104,17 @@ __device__ __forceinline__ void load_strip(Strip<T> &s, const void *base, int64_
 #pragma unroll
   for (int i = 0; i < (int)(sizeof(Strip<T>) / 16); ++i) s.v[i] = ld_nt16(p + 16 * i);
 }
+// keep a strip (ok) or zero it, without a branch
+template <class T> __device__ __forceinline__ void mask_strip(Strip<T> &s, bool ok) {
+  const uint32_t m = ok ? ~0u : 0u;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(Strip<T>) / 16); ++i) {
+    s.v[i].x &= m;
+    s.v[i].y &= m;
+    s.v[i].z &= m;
+    s.v[i].w &= m;
+  }
+}
 template <class T> __device__ __forceinline__ void zero_strip(Strip<T> &s) {
 #pragma unroll
   for (int i = 0; i < (int)(sizeof(Strip<T>) / 16); ++i) s.v[i] = make_uint4(0, 0, 0, 0);
@@ -259,17 +270,19 @@ struct Stats {
 };
 
 // Chan et al. pairwise merge. Callers always pass the partner from the lower lane / wave /
-// workgroup as `a`, so both partners compute bit-identical results.
+// workgroup as `a`, so both partners compute bit-identical results. Branch-free: the weight
+// b.n / n is taken with the hardware reciprocal, and an empty side leaves the other unchanged.
 __device__ __forceinline__ Stats chan_merge(const Stats &a, const Stats &b) {
   const float n = a.n + b.n;
-  if (b.n == 0.0f) return a;
-  if (a.n == 0.0f) return b;
   const float d = b.mean - a.mean;
-  const float fb = b.n / n;
+  const float fb = b.n * __builtin_amdgcn_rcpf(n);
   Stats r;
   r.n = n;
   r.mean = fmaf(d, fb, a.mean);
   r.m2 = a.m2 + b.m2 + d * d * (a.n * fb);
+  const bool a_only = b.n == 0.0f, b_only = a.n == 0.0f;
+  r.mean = a_only ? a.mean : (b_only ? b.mean : r.mean);
+  r.m2 = a_only ? a.m2 : (b_only ? b.m2 : r.m2);
   return r;
 }
 
@@ -280,10 +293,12 @@ __device__ __forceinline__ int lane_id() {
 // wave-wide Chan merge; partner order fixed by lane position
 __device__ __forceinline__ Stats wave_merge(Stats s) {
   const int lane = lane_id();
-#define NF8_STEP(FN, LOW)                                   \
-  {                                                         \
-    Stats o{FN(s.n), FN(s.mean), FN(s.m2)};                 \
-    s = (LOW) ? chan_merge(s, o) : chan_merge(o, s);        \
+#define NF8_STEP(FN, LOW)                                                              \
+  {                                                                                    \
+    const Stats o{FN(s.n), FN(s.mean), FN(s.m2)};                                      \
+    const bool lo = (LOW);                                                             \
+    s = chan_merge(Stats{lo ? s.n : o.n, lo ? s.mean : o.mean, lo ? s.m2 : o.m2},       \
+                   Stats{lo ? o.n : s.n, lo ? o.mean : s.mean, lo ? o.m2 : s.m2});      \
   }
   NF8_STEP(xor1, (lane & 1) == 0)
   NF8_STEP(xor2, (lane & 2) == 0)

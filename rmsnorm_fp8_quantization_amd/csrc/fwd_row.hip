@@ -47,8 +47,13 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   const int fmt = p.out_dtype;
 
   bool cv[KC];
+  float n_in = 0.0f;  // this lane's elements inside the row
 #pragma unroll
-  for (int k = 0; k < KC; ++k) cv[k] = 8 * (int64_t)(tl + TEAM * k) < H;
+  for (int k = 0; k < KC; ++k) {
+    cv[k] = 8 * (int64_t)(tl + TEAM * k) < H;
+    n_in += cv[k] ? 8.0f : 0.0f;
+  }
+  const float n_out = 8.0f * KC - n_in;  // zeroed strip elements
 
   // ---- weights
   __shared__ float wlds[WL == 1 ? NW * COVER : 1];
@@ -164,25 +169,26 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
     const int64_t row = base + team;
     const bool rv = row < p.rows;
     if constexpr (PF) load_row(nxt, base + stride + team);
+    if (H != COVER) {  // strips past the end of the row read column 0: zero them
 #pragma unroll
-    for (int k = 0; k < KC; ++k)
-      if (!(rv && cv[k])) zero_strip<IN>(cur[k]);
+      for (int k = 0; k < KC; ++k) mask_strip<IN>(cur[k], cv[k]);
+    }
 
     // ---- lane-local statistics over its valid strips
     Stats st{0.0f, 0.0f, 0.0f};
-    if constexpr (NORM == NT_LAYERNORM) {
-      float sm = 0.0f, n = 0.0f;
+    if constexpr (NORM == NT_LAYERNORM && P == 1) {
+      // one wave holds the row: the exact two-pass form, mean first, then the sum of squared
+      // deviations from it (strips past the end are zero; each adds mean^2 per element to
+      // the second sum, taken off again)
+      float sm = 0.0f;
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
         float xv[8];
         strip_to_f32<IN>(cur[k], xv);
-        if (rv && cv[k]) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) sm += xv[i];
-          n += 8.0f;
-        }
+        for (int i = 0; i < 8; ++i) sm += xv[i];
       }
-      const float m = n > 0.0f ? sm / n : 0.0f;
+      const float m = wave_sum(sm) * inv_h;
       if constexpr (RECONV) {
 #pragma unroll
         for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
@@ -192,14 +198,42 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
       for (int k = 0; k < KC; ++k) {
         float xv[8];
         strip_to_f32<IN>(cur[k], xv);
-        if (rv && cv[k]) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float d = xv[i] - m;
-            q = fmaf(d, d, q);
-          }
+        for (int i = 0; i < 8; ++i) {
+          const float d = xv[i] - m;
+          q = fmaf(d, d, q);
         }
       }
+      q = fmaf(-n_out * m, m, q);
+      st = Stats{(float)H, m, wave_sum(q)};
+    } else if constexpr (NORM == NT_LAYERNORM) {
+      // several waves per row: per-lane (n, mean, M2), merged in the Chan form
+      float sm = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float xv[8];
+        strip_to_f32<IN>(cur[k], xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm += xv[i];
+      }
+      const float n = n_in;
+      const float m = n > 0.0f ? sm * __builtin_amdgcn_rcpf(n) : 0.0f;
+      if constexpr (RECONV) {
+#pragma unroll
+        for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
+      }
+      float q = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float xv[8];
+        strip_to_f32<IN>(cur[k], xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float d = xv[i] - m;
+          q = fmaf(d, d, q);
+        }
+      }
+      q = fmaf(-n_out * m, m, q);
       st = wave_merge(Stats{n, m, q});
     } else {
       float q = 0.0f;
