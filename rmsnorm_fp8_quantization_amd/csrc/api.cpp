@@ -260,7 +260,7 @@ int plan_bwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_t
   const int64_t gmax = (int64_t)kMaxCus * bwd_wgs_per_cu(cfg);
   pl->G_max = rows < gmax ? (rows > 0 ? rows : 1) : gmax;
   const int arrays = norm_type == NORM_LAYERNORM ? 2 : 1;
-  pl->ws_bytes = kWsHeaderBytes + round_up((size_t)pl->G_max * hidden * arrays * sizeof(float), 256);
+  pl->ws_bytes = kWsHeaderBytes + round_up((size_t)pl->G_max * round_up((size_t)hidden, 32) * arrays * sizeof(float), 256);
   return NORM_OK;
 }
 

@@ -162,48 +162,54 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
     if constexpr (!PF) load_row(a, row + 2 * G);
   }
 
-  // this workgroup's partial weight gradients
+  // this workgroup's partial weight gradients, into the column-block-major layout
+  // [H32 / 32][G][32] (H32 = hidden rounded up to 32): each 32-column block's G partials are
+  // contiguous, so the finalize kernel streams them
+  const int64_t arr = (int64_t)p.G * ((H + 31) & ~(int64_t)31);
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
     if (!cv[k]) continue;
     const int64_t col = 8 * (int64_t)(tid + NT * k);
-    float4 *dst = reinterpret_cast<float4 *>(p.part + (int64_t)blockIdx.x * H + col);
+    const int64_t at = ((col >> 5) * p.G + blockIdx.x) * 32 + (col & 31);
+    float4 *dst = reinterpret_cast<float4 *>(p.part + at);
     dst[0] = make_float4(dg[k][0], dg[k][1], dg[k][2], dg[k][3]);
     dst[1] = make_float4(dg[k][4], dg[k][5], dg[k][6], dg[k][7]);
     if constexpr (NORM == NT_LAYERNORM) {
-      float4 *dsb = reinterpret_cast<float4 *>(p.part + ((int64_t)p.G + blockIdx.x) * H + col);
+      float4 *dsb = reinterpret_cast<float4 *>(p.part + arr + at);
       dsb[0] = make_float4(db[k][0], db[k][1], db[k][2], db[k][3]);
       dsb[1] = make_float4(db[k][4], db[k][5], db[k][6], db[k][7]);
     }
   }
 }
 
-// Fixed-order reduction of the G partial rows. Workgroup (x, y) owns 32 columns of array y
-// (0: dgamma, 1: dbeta); thread (c, q) adds 4 columns (one float4) of partial rows q, q + 32,
-// q + 64, ... with four loads in flight, and the 32 sums per column are added in q order. The
-// grid has H / 32 workgroups per array so the whole chip streams the partials.
+// Fixed-order reduction of the G partials. Workgroup (x, y) owns column block x (32 columns)
+// of array y (0: dgamma, 1: dbeta), whose G partials are one contiguous [G][32] slab; thread
+// (c, q) adds 4 columns (one float4) of partials q, q + 32, q + 64, ... with four loads in
+// flight (each load instruction reads 4 KB of the slab), and the 32 sums per column are added
+// in q order. The grid has ceil(H / 32) workgroups per array.
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(FinalizeParams p) {
   constexpr int Q = 32;
   const int c = threadIdx.x & 7;
   const int q = threadIdx.x >> 3;
   const int64_t col = (int64_t)blockIdx.x * 32 + 4 * c;
   const int which = blockIdx.y;
-  const float *part = p.part + (int64_t)which * p.G * p.hidden;
+  const int64_t arr = (int64_t)p.G * ((p.hidden + 31) & ~(int64_t)31);
+  const float *part = p.part + which * arr + (int64_t)blockIdx.x * p.G * 32 + 4 * c;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (col < p.hidden) {
     int g = q;
     for (; g + 3 * Q < p.G; g += 4 * Q) {
-      const float4 a = *reinterpret_cast<const float4 *>(part + (int64_t)g * p.hidden + col);
-      const float4 b = *reinterpret_cast<const float4 *>(part + (int64_t)(g + Q) * p.hidden + col);
-      const float4 e = *reinterpret_cast<const float4 *>(part + (int64_t)(g + 2 * Q) * p.hidden + col);
-      const float4 f = *reinterpret_cast<const float4 *>(part + (int64_t)(g + 3 * Q) * p.hidden + col);
+      const float4 a = *reinterpret_cast<const float4 *>(part + (int64_t)g * 32);
+      const float4 b = *reinterpret_cast<const float4 *>(part + (int64_t)(g + Q) * 32);
+      const float4 e = *reinterpret_cast<const float4 *>(part + (int64_t)(g + 2 * Q) * 32);
+      const float4 f = *reinterpret_cast<const float4 *>(part + (int64_t)(g + 3 * Q) * 32);
       s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
       s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
       s.x += e.x; s.y += e.y; s.z += e.z; s.w += e.w;
       s.x += f.x; s.y += f.y; s.z += f.z; s.w += f.w;
     }
     for (; g < p.G; g += Q) {
-      const float4 a = *reinterpret_cast<const float4 *>(part + (int64_t)g * p.hidden + col);
+      const float4 a = *reinterpret_cast<const float4 *>(part + (int64_t)g * 32);
       s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
     }
   }

@@ -261,7 +261,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
     }
 
     const float mu = NORM == NT_LAYERNORM ? st.mean : 0.0f;
-    const float rs = 1.0f / sqrtf(st.m2 * inv_h + p.eps);
+    const float rs = __builtin_amdgcn_rsqf(st.m2 * inv_h + p.eps);
     if constexpr (RECONV) {
 #pragma unroll
       for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);

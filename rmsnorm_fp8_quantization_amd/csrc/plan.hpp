@@ -107,7 +107,8 @@ struct FwdTileParams {
 // ---- backward ------------------------------------------------------------------------------
 // A workgroup of W waves handles one row at a time (all lanes of the workgroup on one row),
 // loops over rows g, g + G, ...; lane owns KC strips (columns 8 * (tid + 64 * W * k)).
-// Partial weight gradients of workgroup g go to part[g, :] (and part[G + g, :] for dbeta).
+// Partial weight gradients of workgroup g, column j go to part[(j / 32) * G + g][j % 32] of a
+// [ceil(hidden / 32)][G][32] array (a second one follows for dbeta).
 struct BwdParams {
   const void *dy;
   const void *x;
@@ -116,7 +117,7 @@ struct BwdParams {
   const float *rsigma;
   const void *gamma;
   void *dx;
-  float *part;           // [G or 2G, hidden]
+  float *part;           // 1 or 2 arrays [ceil(hidden / 32)][G][32]
   int64_t rows;
   int64_t hidden;
   int w_dtype;
@@ -125,7 +126,7 @@ struct BwdParams {
 };
 
 struct FinalizeParams {
-  const float *part;  // [nparts, hidden]
+  const float *part;  // 1 or 2 arrays [ceil(hidden / 32)][G][32]
   void *dgamma;
   void *dbeta;        // LayerNorm or nullptr
   int64_t hidden;
