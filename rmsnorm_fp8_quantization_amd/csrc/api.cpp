@@ -228,7 +228,7 @@ struct BwdPlan {
 constexpr int kMaxCus = 256;  // gfx950 (MI355X) compute units; bounds the workspace query
 
 int bwd_wgs_per_cu(int cfg) {
-  const int w = kBwdShapes[cfg].W;
+  const int w = kBwdShapes[cfg].W * kBwdShapes[cfg].T;
   return w >= 8 ? 1 : 8 / w;
 }
 

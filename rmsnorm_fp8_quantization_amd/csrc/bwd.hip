@@ -19,12 +19,13 @@
 
 namespace nf8 {
 
-template <int NORM, class IN, bool ADD, int W, int KC>
-__global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
-  constexpr int NT = 64 * W;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+template <int NORM, class IN, bool ADD, int W, int KC, int T>
+__global__ __launch_bounds__(64 * W * T) void bwd_kernel(BwdParams p) {
+  constexpr int NT = 64 * W;  // threads of one team (one row)
+  const int lane = threadIdx.x & 63;
+  const int team = (int)threadIdx.x / NT;
+  const int tid = (int)threadIdx.x - team * NT;  // thread within the team
+  const int wave = tid >> 6;                      // wave within the team
   const int64_t H = p.hidden;
 
   bool cv[KC];
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
     }
   }
 
-  __shared__ float red[2][W][2];
+  __shared__ float red[2][T][W][2];
   const float inv_h = 1.0f / (float)H;
 
   // The next row's dy, x (and residual) are loaded while the current row is processed. The
@@ -61,7 +62,8 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
     Strip<IN> dys[KC], xs[KC], rsd[ADD ? KC : 1];
     float rs, mu;
   };
-  auto load_row = [&](RowData &d, int64_t row) {
+  auto load_row = [&](RowData &d, int64_t base) {
+    const int64_t row = base + team;
     const int64_t r = row < p.rows ? row : 0;
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
@@ -75,7 +77,9 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
   };
 
   // one row: statistics, dx, and the weight-gradient partial sums
-  auto step = [&](RowData &cur, int64_t row, int iter) {
+  auto step = [&](RowData &cur, int64_t base, int iter) {
+    const int64_t row = base + team;
+    const bool rv = row < p.rows;  // a team past the last row adds nothing and stores nothing
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       if (!cv[k]) {
@@ -83,6 +87,7 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
         zero_strip<IN>(cur.xs[k]);
         if constexpr (ADD) zero_strip<IN>(cur.rsd[k]);
       }
+      if constexpr (T > 1) mask_strip<IN>(cur.dys[k], rv);
     }
     const Strip<IN> *const dys = cur.dys;
     const Strip<IN> *const xs = cur.xs;
@@ -109,16 +114,16 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
     s2 = wave_sum(s2);
     if constexpr (W > 1) {
       if (lane == 0) {
-        red[iter & 1][wave][0] = s1;
-        red[iter & 1][wave][1] = s2;
+        red[iter & 1][team][wave][0] = s1;
+        red[iter & 1][team][wave][1] = s2;
       }
       __syncthreads();
-      s1 = red[iter & 1][0][0];
-      s2 = red[iter & 1][0][1];
+      s1 = red[iter & 1][team][0][0];
+      s2 = red[iter & 1][team][0][1];
 #pragma unroll
       for (int w = 1; w < W; ++w) {
-        s1 += red[iter & 1][w][0];
-        s2 += red[iter & 1][w][1];
+        s1 += red[iter & 1][team][w][0];
+        s2 += red[iter & 1][team][w][1];
       }
     }
     const float c1 = NORM == NT_LAYERNORM ? s1 * inv_h : 0.0f;
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
         dg[k][i] = fmaf(dv[i], xh, dg[k][i]);
         if constexpr (NORM == NT_LAYERNORM) db[k][i] += dv[i];
       }
-      if (cv[k]) store_t8<IN>(p.dx, row * H + 8 * (int64_t)(tid + NT * k), out);
+      if (rv && cv[k]) store_t8<IN>(p.dx, row * H + 8 * (int64_t)(tid + NT * k), out);
     }
   };
 
@@ -149,10 +154,12 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
   // row's registers. (Not for 16 waves x 2 strips: two rows of inputs would not fit the
   // register budget; those load each row after the previous one is done.)
   constexpr bool PF = !(W == 16 && KC >= 2);
-  const int64_t G = gridDim.x;
+  // (T teams walk rows base + team in step, so every team makes the same number of steps and
+  // meets every barrier)
+  const int64_t G = (int64_t)gridDim.x * T;
   RowData a, b;
-  load_row(a, blockIdx.x);
-  for (int64_t row = blockIdx.x, iter = 0; row < p.rows; row += 2 * G, iter += 2) {
+  load_row(a, (int64_t)blockIdx.x * T);
+  for (int64_t row = (int64_t)blockIdx.x * T, iter = 0; row < p.rows; row += 2 * G, iter += 2) {
     if constexpr (PF) load_row(b, row + G);
     step(a, row, (int)iter);
     if (row + G >= p.rows) break;
@@ -160,6 +167,37 @@ __global__ __launch_bounds__(64 * W) void bwd_kernel(BwdParams p) {
     else load_row(b, row + G);
     step(b, row + G, (int)iter + 1);
     if constexpr (!PF) load_row(a, row + 2 * G);
+  }
+
+  // the teams' weight-gradient sums, added in team order (deterministic)
+  if constexpr (T > 1) {
+    constexpr int NW = NORM == NT_LAYERNORM ? 2 : 1;
+    __shared__ __align__(16) float tpart[T > 1 ? (T - 1) * NW * KC * 8 * NT : 1];
+    if (team > 0) {
+      float *d = tpart + (size_t)(team - 1) * NW * KC * 8 * NT;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          d[(k * 8 + i) * NT + tid] = dg[k][i];
+          if constexpr (NORM == NT_LAYERNORM) d[((KC + k) * 8 + i) * NT + tid] = db[k][i];
+        }
+      }
+    }
+    __syncthreads();
+    if (team > 0) return;
+#pragma unroll
+    for (int t = 1; t < T; ++t) {
+      const float *d = tpart + (size_t)(t - 1) * NW * KC * 8 * NT;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dg[k][i] += d[(k * 8 + i) * NT + tid];
+          if constexpr (NORM == NT_LAYERNORM) db[k][i] += d[((KC + k) * 8 + i) * NT + tid];
+        }
+      }
+    }
   }
 
   // this workgroup's partial weight gradients, into the column-block-major layout
@@ -243,17 +281,20 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(FinalizeParams p) {
 
 template <int NORM, class IN, bool ADD>
 static const void *pick_bwd_cfg(int cfg) {
+#define NF8_BWD(C) \
+  (const void *)bwd_kernel<NORM, IN, ADD, kBwdShapes[C].W, kBwdShapes[C].KC, kBwdShapes[C].T>
   switch (cfg) {
-    case BWD_W2_K1: return (const void *)bwd_kernel<NORM, IN, ADD, 2, 1>;
-    case BWD_W4_K1: return (const void *)bwd_kernel<NORM, IN, ADD, 4, 1>;
-    case BWD_W4_K2: return (const void *)bwd_kernel<NORM, IN, ADD, 4, 2>;
-    case BWD_W8_K2: return (const void *)bwd_kernel<NORM, IN, ADD, 8, 2>;
-    case BWD_W16_K2: return (const void *)bwd_kernel<NORM, IN, ADD, 16, 2>;
-    case BWD_W8_K1: return (const void *)bwd_kernel<NORM, IN, ADD, 8, 1>;
-    case BWD_W16_K1: return (const void *)bwd_kernel<NORM, IN, ADD, 16, 1>;
-    case BWD_W4_K4: return (const void *)bwd_kernel<NORM, IN, ADD, 4, 4>;
+    case BWD_W2_K1: return NF8_BWD(BWD_W2_K1);
+    case BWD_W4_K1: return NF8_BWD(BWD_W4_K1);
+    case BWD_W4_K2: return NF8_BWD(BWD_W4_K2);
+    case BWD_W8_K2: return NF8_BWD(BWD_W8_K2);
+    case BWD_W16_K2: return NF8_BWD(BWD_W16_K2);
+    case BWD_W8_K1: return NF8_BWD(BWD_W8_K1);
+    case BWD_W16_K1: return NF8_BWD(BWD_W16_K1);
+    case BWD_W4_K4: return NF8_BWD(BWD_W4_K4);
     default: return nullptr;
   }
+#undef NF8_BWD
 }
 
 template <int NORM, bool ADD>

@@ -51,12 +51,18 @@ enum BwdCfg : int {
   BWD_W4_K4,
   BWD_NCFG
 };
+// T teams of W waves per workgroup, each team on its own row; the teams share one partial
+// row of weight gradients, so the workgroup count (and the partial traffic) stays one per CU
 struct BwdShape {
-  int W, KC;
-  int threads() const { return 64 * W; }
-  int64_t cover() const { return 512LL * W * KC; }
+  int W, KC, T;
+  constexpr int threads() const { return 64 * W * T; }
+  constexpr int64_t cover() const { return 512LL * W * KC; }
 };
-constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1}, {4, 1}, {4, 2}, {8, 2}, {16, 2}, {8, 1}, {16, 1}, {4, 4}};
+#ifndef NF8_BWD_T4K2
+#define NF8_BWD_T4K2 2
+#endif
+constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1, 4}, {4, 1, 2}, {4, 2, NF8_BWD_T4K2}, {8, 2, 1},
+                                           {16, 2, 1}, {8, 1, 1}, {16, 1, 1}, {4, 4, 1}};
 
 // ---- forward tile kernel (second pass of a columnwise output): 8 waves, 128 x 128 tiles
 constexpr int kColTileRows = 128;
