@@ -133,15 +133,27 @@ def fp8_quantize(v, fmt: Format):
     return fp8_encode(round_nearest_even(v, fmt), fmt)
 
 
-def e8m0_exponent(a, fp8_name: str):
+def e8m0_exponent(a, fp8_name: str, rule: str = "floor"):
     """Shared MX block exponent X for a block whose largest magnitude is ``a`` (float64).
 
-    X = floor(log2 a) - emax(element), clamped to the E8M0 range [-127, 127];
-    an all-zero block takes the smallest scale, X = -127.  The stored byte is X + 127.
+    rule "floor" (the OCP MX rule): X = floor(log2 a) - emax(element).
+    rule "ceil": the smallest X with a * 2**-X <= the element format's largest finite value
+    (448 for E4M3, 57344 for E5M2), i.e. X = ceil(log2(a / max)), so no element of the block
+    saturates.  Both largest values are 1.75 * 2**emax, so with a = m * 2**E (m in [1, 2))
+    this is E - emax, plus one when m > 1.75.
+    Either way X is clamped to the E8M0 range [-127, 127]; an all-zero block takes the
+    smallest scale, X = -127.  The stored byte is X + 127.
     """
     a = np.asarray(a, dtype=np.float64)
     pos = a > 0
-    x = np.where(pos, floor_log2(np.where(pos, a, 1.0)) - MX_EMAX[fp8_name], -127)
+    safe = np.where(pos, a, 1.0)
+    x = floor_log2(safe) - MX_EMAX[fp8_name]
+    if rule == "ceil":
+        m = safe / np.ldexp(1.0, floor_log2(safe))          # significand in [1, 2), exact
+        x = x + (m > 1.75)
+    elif rule != "floor":
+        raise ValueError(f"unknown E8M0 rule {rule!r}")
+    x = np.where(pos, x, -127)
     return np.clip(x, -127, 127).astype(np.int64)
 
 

@@ -131,9 +131,10 @@ def delayed_epilogue(v, scale: float, amax_in: float, fp8: str, colwise: bool):
     return out
 
 
-def mx_quantize_rows(v, fp8: str, block: int = 32):
+def mx_quantize_rows(v, fp8: str, block: int = 32, rule: str = "floor"):
     """MXFP8 along the last axis: blocks of ``block`` consecutive elements share one
-    E8M0 scale.  The last block of a row may be shorter.
+    E8M0 scale (exponent rule ``rule``, see e8m0_exponent).  The last block of a row may be
+    shorter.
 
     Returns (codes uint8 [r, c], scale bytes uint8 [r, ceil(c / block)])."""
     fmt = FORMATS[fp8]
@@ -146,22 +147,22 @@ def mx_quantize_rows(v, fp8: str, block: int = 32):
     for b in range(nb):
         blk = y32[:, b * block:(b + 1) * block]
         a = np.max(np.abs(blk), axis=1) if blk.shape[1] else np.zeros(r)
-        x = e8m0_exponent(a, fp8)
+        x = e8m0_exponent(a, fp8, rule)
         scales[:, b] = (x + 127).astype(np.uint8)
         scaled = blk * np.ldexp(1.0, (-x)[:, None])       # exact power-of-two scaling
         codes[:, b * block:(b + 1) * block] = fp8_quantize(round_nearest_even(scaled, FP32), fmt)
     return codes, scales
 
 
-def mx_epilogue(v, fp8: str, colwise: bool, block: int = 32):
+def mx_epilogue(v, fp8: str, colwise: bool, block: int = 32, rule: str = "floor"):
     """MXFP8 outputs: rowwise data [rows, hidden] + scales [rows, ceil(hidden/32)];
     colwise data [hidden, rows] + scales [hidden, ceil(rows/32)] (blocks of 32
     consecutive rows of one column)."""
     out = {}
-    out["rowwise"], out["rowwise_scale"] = mx_quantize_rows(v, fp8, block)
+    out["rowwise"], out["rowwise_scale"] = mx_quantize_rows(v, fp8, block, rule)
     if colwise:
         vt = np.ascontiguousarray(np.asarray(v).T)
-        out["colwise"], out["colwise_scale"] = mx_quantize_rows(vt, fp8, block)
+        out["colwise"], out["colwise_scale"] = mx_quantize_rows(vt, fp8, block, rule)
     return out
 
 

@@ -196,3 +196,72 @@ def test_mx_scaled_block_max_lies_in_top_binade():
         s = a * np.ldexp(1.0, -x)
         emax = F.MX_EMAX[name]
         assert np.all(s >= 2.0 ** emax) and np.all(s < 2.0 ** (emax + 1))
+
+
+def test_e8m0_ceil_golden_examples():
+    n = 0
+    with open(os.path.join(GOLDEN, "mx_e8m0_ceil_examples.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            parts = line.split()
+            if parts[0] == "code":
+                _, name, amax, elem, code = parts
+                x = int(F.e8m0_exponent(np.array([float(amax)]), name, "ceil")[0])
+                scaled = float(elem) * 2.0 ** (-x)
+                assert int(F.fp8_quantize(np.array([scaled]), F.FORMATS[name])[0]) == int(code, 16), line
+            else:
+                name, amax, byte = parts
+                assert int(F.e8m0_exponent(np.array([float(amax)]), name, "ceil")[0]) + 127 == int(byte), line
+            n += 1
+    assert n >= 15
+
+
+@pytest.mark.parametrize("name", ["e4m3", "e5m2"])
+def test_e8m0_ceil_is_the_smallest_exponent_that_does_not_saturate(name):
+    """Brute force: X is the smallest integer with a * 2^-X <= max, checked by trying X and
+    X - 1 in exact power-of-two arithmetic, on random maxima and on the boundaries
+    1.75 * 2^k (where the significand equals that of the largest finite value) and their
+    float64 neighbours."""
+    fmax = F.FORMATS[name].max_finite
+    rng = np.random.default_rng(3)
+    k = np.arange(-100, 100)
+    edge = np.ldexp(1.75, k)
+    a = np.concatenate([np.exp(rng.uniform(-60, 60, 50000)), edge, np.nextafter(edge, 0.0),
+                        np.nextafter(edge, np.inf), np.ldexp(1.0, k), np.nextafter(np.ldexp(1.0, k), 0.0)])
+    x = F.e8m0_exponent(a, name, "ceil")
+    assert np.all(a * np.ldexp(1.0, -x) <= fmax)
+    assert np.all(a * np.ldexp(1.0, -(x - 1)) > fmax)
+    # exactly on the boundary the scaled maximum is the largest finite value itself
+    xe = F.e8m0_exponent(edge, name, "ceil")
+    assert np.all(edge * np.ldexp(1.0, -xe) == fmax)
+
+
+@pytest.mark.parametrize("name", ["e4m3", "e5m2"])
+def test_e8m0_ceil_vs_floor(name):
+    """The rules differ by one exactly when the significand of a exceeds 1.75."""
+    rng = np.random.default_rng(4)
+    a = np.exp(rng.uniform(-60, 60, 100000))
+    xf = F.e8m0_exponent(a, name)
+    xc = F.e8m0_exponent(a, name, "ceil")
+    m, _ = np.frexp(a)                       # a = m * 2^e, m in [0.5, 1)
+    assert np.array_equal(xc - xf, (2.0 * m > 1.75).astype(np.int64))
+    assert int(F.e8m0_exponent(np.array([0.0]), name, "ceil")[0]) == -127
+    assert int(F.e8m0_exponent(np.array([1e300]), name, "ceil")[0]) == 127
+
+
+def test_mx_ceil_rule_never_saturates():
+    """Under the ceil rule every scaled element is within the finite range before rounding,
+    so no code is produced by saturation: the codes equal the unclamped nearest rounding."""
+    from oracle.norm import mx_quantize_rows
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((64, 96)) * np.exp(rng.uniform(-8, 8, (64, 1)))
+    for name in ("e4m3", "e5m2"):
+        fmt = F.FORMATS[name]
+        codes, scales = mx_quantize_rows(v, name, rule="ceil")
+        x = scales.astype(np.int64) - 127
+        y32 = F.to_f32(v)
+        for b in range(3):
+            s = y32[:, 32 * b:32 * b + 32] * np.ldexp(1.0, -x[:, b])[:, None]
+            assert np.all(np.abs(s) <= fmt.max_finite)
+            assert np.array_equal(codes[:, 32 * b:32 * b + 32], F.fp8_quantize(s, fmt))
