@@ -68,7 +68,8 @@ typedef enum {
 typedef enum {
   NORM_SCALING_NONE = 0,
   NORM_SCALING_DELAYED_TENSOR = 1,
-  NORM_SCALING_MXFP8_1D32 = 2 /* 32-element blocks, one E8M0 scale byte per block */
+  NORM_SCALING_MXFP8_1D32 = 2,     /* 32-element blocks, one E8M0 scale byte per block */
+  NORM_SCALING_MXFP8_1D32_CEIL = 3 /* the same blocks, exponent rounded up: no element saturates */
 } norm_scaling_t;
 
 /* [XLA-Norm] Signature / Description: rowwise output with optional columnwise output. */
@@ -128,6 +129,10 @@ int norm_bwd_workspace_size(int64_t rows, int64_t hidden, int in_dtype, int w_dt
  *     Rowwise: y [rows, hidden] codes, scale_inv = uint8 [rows, ceil(hidden/32)] bytes X+127.
  *     Columnwise: y_colwise [hidden, rows] codes, colwise_scale_inv = uint8
  *     [hidden, ceil(rows/32)]. scale, amax, updated_amax unused (NULL).
+ *   scaling == NORM_SCALING_MXFP8_1D32_CEIL: as NORM_SCALING_MXFP8_1D32, except that X is the
+ *     smallest integer with amax_block * 2^-X <= the format's largest finite value (448 for
+ *     E4M3, 57344 for E5M2), clamped to [-127, 127], so no code saturates. The pages leave the
+ *     exponent rule of their MXFP8 mode open; the floor rule is the default reading.
  *   The layout pointers not requested by qlayout must be NULL.
  *
  *   Errors: NORM_ERR_INVALID_ARG for NULL required pointers or bad codes; NORM_ERR_UNSUPPORTED

@@ -150,6 +150,7 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
       break;
     case NORM_SCALING_DELAYED_TENSOR:
     case NORM_SCALING_MXFP8_1D32:
+    case NORM_SCALING_MXFP8_1D32_CEIL:
       if (!is_fp8(out_dtype)) return fail(NORM_ERR_UNSUPPORTED, "scaled output must be FP8_E4M3 or FP8_E5M2");
       pl->mode = scaling == NORM_SCALING_DELAYED_TENSOR ? MODE_DELAYED : MODE_MX;
       break;
@@ -374,6 +375,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   f.mx_cols = cdiv(hidden, 32);
   f.w_dtype = w_dtype;
   f.out_dtype = out_dtype;
+  f.mx_ceil = scaling == NORM_SCALING_MXFP8_1D32_CEIL ? 1 : 0;
   f.zero_centered = zero_centered_gamma ? 1 : 0;
   f.eps = epsilon;
 

@@ -203,9 +203,15 @@ __device__ __forceinline__ uint2 fp8_pack8(const float (&u)[8], int fmt) {
 // MXFP8 shared exponent X of a block whose largest magnitude is `a` (float32, a >= 0):
 // X = clamp(floor(log2 a) - emax, -127, 127); a zero or subnormal maximum gives -127.
 // floor(log2 a) of a normal float32 is its unbiased exponent field.
-__device__ __forceinline__ int mx_exponent(float a, int fmt) {
+__device__ __forceinline__ int mx_exponent(float a, int fmt, int ceil_rule) {
+  // floor rule: X = floor(log2 a) - emax. Round-up rule (ceil_rule != 0): the smallest X with
+  // a * 2^-X <= the format's largest finite value (1.75 * 2^emax for E4M3 and E5M2), i.e. one
+  // more when a's significand exceeds 1.75 (binary32 fraction bits above 0x600000).
+  const uint32_t b = __float_as_uint(a);
   const int emax = fmt == DT_E4M3 ? 8 : 15;
-  int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127 - emax;
+  const int ef = (int)((b >> 23) & 0xffu);
+  int e = ef - 127 - emax;
+  if (ceil_rule && ef != 0 && (b & 0x7fffffu) > 0x600000u) e += 1;
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 // 2^-X as float32 (X in [-127, 127] keeps the biased exponent 127 - X in [0, 254]; X = 127 gives

@@ -330,7 +330,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
         for (int i = 0; i < 8; ++i) {
           const int c = 8 * (lane + 64 * k) + i;
           const float a = fmaxf(fmaxf(colmax[0][c], colmax[1][c]), fmaxf(colmax[2][c], colmax[3][c]));
-          colx[i] = mx_exponent(a, fmt);
+          colx[i] = mx_exponent(a, fmt, p.mx_ceil);
           colf[i] = exp2_neg(colx[i]);
         }
       }
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[i]));
             a = quad_max(ok ? a : 0.0f);
-            const int X = mx_exponent(a, fmt);
+            const int X = mx_exponent(a, fmt, p.mx_ceil);
             const float f = exp2_neg(X);
             float u[8];
 #pragma unroll

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
       for (int i = 0; i < 8; ++i) {
         float a = fmaxf(cm[i], om[i]);
         if constexpr (NORM != NT_LAYERNORM) a = a * fabsf(gk[i]);
-        const int X = mx_exponent(a, fmt);
+        const int X = mx_exponent(a, fmt, p.mx_ceil);
         colf[i] = exp2_neg(X);
         if (rg == 0 && (wave & 1) == 0) colx[wave >> 1][cloc + i] = (uint8_t)(X + 127);
       }
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
 #pragma unroll
           for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[i]));
           a = quad_max(ok ? a : 0.0f);  // 4 lanes = one 32-column block
-          const int X = mx_exponent(a, fmt);
+          const int X = mx_exponent(a, fmt, p.mx_ceil);
           const float f = exp2_neg(X);
           float u[8];
 #pragma unroll

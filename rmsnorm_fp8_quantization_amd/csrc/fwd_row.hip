@@ -303,7 +303,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[i]));
         a = quad_max(ok ? a : 0.0f);
-        const int X = mx_exponent(a, fmt);
+        const int X = mx_exponent(a, fmt, p.mx_ceil);
         const float f = exp2_neg(X);
         float u[8];
 #pragma unroll

@@ -68,6 +68,7 @@ struct FwdRowParams {
   int w_dtype;
   int out_dtype;    // plain: F32/F16/BF16; delayed / MX: E4M3/E5M2
   int zero_centered;
+  int mx_ceil;      // MX: round-up exponent rule (no element saturates) instead of floor
   float eps;
 };
 

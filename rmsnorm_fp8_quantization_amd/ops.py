@@ -24,7 +24,7 @@ _DT = {torch.float32: L.NORM_F32, torch.float16: L.NORM_F16, torch.bfloat16: L.N
 _FP8 = {"e4m3": L.NORM_FP8_E4M3, "e5m2": L.NORM_FP8_E5M2}
 _NORM = {"layernorm": L.NORM_LAYERNORM, "rmsnorm": L.NORM_RMSNORM}
 _SCALING = {"none": L.NORM_SCALING_NONE, "delayed": L.NORM_SCALING_DELAYED_TENSOR,
-            "mxfp8": L.NORM_SCALING_MXFP8_1D32}
+            "mxfp8": L.NORM_SCALING_MXFP8_1D32, "mxfp8_ceil": L.NORM_SCALING_MXFP8_1D32_CEIL}
 _LAYOUT = {"rowwise": L.NORM_Q_ROWWISE, "colwise": L.NORM_Q_COLWISE,
            "rowwise_colwise": L.NORM_Q_ROWWISE_COLWISE}
 
@@ -127,7 +127,7 @@ def prepare_fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tenso
         si = torch.empty(1, dtype=torch.float32, device=dev) if rowwise else None
         csi = torch.empty(1, dtype=torch.float32, device=dev) if colwise else None
         upd = amax if amax_inplace else torch.empty(1, dtype=torch.float32, device=dev)
-    elif scaling == "mxfp8":
+    elif scaling in ("mxfp8", "mxfp8_ceil"):
         si = torch.empty(rows, (hidden + 31) // 32, dtype=torch.uint8, device=dev) if rowwise else None
         csi = torch.empty(hidden, (rows + 31) // 32, dtype=torch.uint8, device=dev) if colwise else None
     nbytes = fwd_workspace_size(rows, hidden, x.dtype, gamma.dtype, out_code, norm, scaling, layout,
@@ -149,7 +149,8 @@ def fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor] = Non
     columnwise output: row statistics, then 128 x 128 tiles).
 
     x: [rows, hidden] (f32/f16/bf16); gamma, beta: [hidden]. Keywords: norm ("layernorm" |
-    "rmsnorm"), eps, zero_centered_gamma, scaling ("none" | "delayed" | "mxfp8"), out_dtype
+    "rmsnorm"), eps, zero_centered_gamma, scaling ("none" | "delayed" | "mxfp8" | "mxfp8_ceil": MXFP8 with the round-up exponent
+    rule, no saturation), out_dtype
     (scaling "none"), fp8 ("e4m3" | "e5m2"), scale / amax (float32[1] GPU tensors, delayed
     scaling), layout ("rowwise" | "colwise" | "rowwise_colwise"), cu_margin, amax_inplace.
     Returns ``y`` (rowwise output: out_dtype, or uint8 FP8 codes), ``y_colwise`` ([hidden, rows]

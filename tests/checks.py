@@ -14,9 +14,10 @@ Tolerances (written here, used by every parity test):
                   the value, where terms = |xhat*g| + |mu*rsigma*g| + |beta| -- the same
                   allowance as for bf16 outputs, since the code is decided from a binary32 y)
   E8M0 scales     bit-exact, except blocks whose float64 maximum lies within 2^-19
-                  (relative) of a power of two, where the binary32 maximum may fall on
-                  either side: there either neighbouring exponent is accepted and the
-                  block's codes are checked under the GPU's exponent
+                  (relative) of a decision boundary of the exponent rule (a power of two;
+                  1.75 times a power of two for the round-up rule), where the binary32
+                  maximum may fall on either side: there either neighbouring exponent is
+                  accepted and the block's codes are checked under the GPU's exponent
   amax            |g - v| / v <= 1e-6
   scale_inv       bit-exact
   bf16 / f16 dx   (|g - v| - half_ulp(v)) / max(|v|, rms_row(v)) <= 2e-3: the error beyond
@@ -164,9 +165,11 @@ def check_delayed(out, v, scale, amax_in, fp8, rowwise=True, colwise=False, term
     return rep
 
 
-def check_mx_rows(codes_g, scales_g, v, fp8, what="mx", terms=None):
+def check_mx_rows(codes_g, scales_g, v, fp8, what="mx", terms=None, rule="floor"):
     """MXFP8 blocks along the last axis of v (float64 [r, c]) against GPU codes / scale bytes
-    (terms: LayerNorm term magnitudes laid out like v, see the module docstring)."""
+    (terms: LayerNorm term magnitudes laid out like v, see the module docstring; rule: the
+    E8M0 exponent rule, whose decision boundaries are the powers of two for "floor" and
+    1.75 times the powers of two for "ceil")."""
     fmt = F.FORMATS[fp8]
     v = np.asarray(v, np.float64)
     r, c = v.shape
@@ -181,21 +184,22 @@ def check_mx_rows(codes_g, scales_g, v, fp8, what="mx", terms=None):
         sl = slice(32 * b, min(32 * b + 32, c))
         blk32 = y32[:, sl]
         a64 = np.max(np.abs(v[:, sl]), axis=1)
-        x_ref = F.e8m0_exponent(np.max(np.abs(blk32), axis=1), fp8)
+        x_ref = F.e8m0_exponent(np.max(np.abs(blk32), axis=1), fp8, rule)
         x_g = scales_g[:, b].astype(np.int64) - 127
         bad = x_g != x_ref
         if bad.any():
-            # allowed only next to a power of two, and only by one step
-            k = np.floor(np.log2(np.where(a64 > 0, a64, 1.0)))
-            near = (np.abs(a64 - 2.0 ** k) <= TOL["e8m0_window"] * a64) | \
-                   (np.abs(a64 - 2.0 ** (k + 1)) <= TOL["e8m0_window"] * a64)
+            # allowed only next to a decision boundary of the rule, and only by one step
+            base = 1.75 if rule == "ceil" else 1.0
+            k = np.floor(np.log2(np.where(a64 > 0, a64, 1.0) / base))
+            lo_edge, hi_edge = base * 2.0 ** k, base * 2.0 ** (k + 1)
+            near = (np.abs(a64 - lo_edge) <= TOL["e8m0_window"] * a64) | \
+                   (np.abs(a64 - hi_edge) <= TOL["e8m0_window"] * a64)
             if not np.all(near[bad] & (np.abs(x_g - x_ref)[bad] == 1)):
-                kk = k[bad]
-                dist = np.minimum(np.abs(a64[bad] - 2.0 ** kk), np.abs(a64[bad] - 2.0 ** (kk + 1))) / a64[bad]
+                dist = np.minimum(np.abs(a64 - lo_edge), np.abs(a64 - hi_edge))[bad] / a64[bad]
                 raise AssertionError(
                     f"{what} block {b}: {int(bad.sum())} E8M0 scales differ: rows {np.nonzero(bad)[0][:8]}, "
                     f"gpu X {x_g[bad][:8]}, oracle X {x_ref[bad][:8]}, block max {a64[bad][:8]}, "
-                    f"relative distance to a power of two {dist[:8]}")
+                    f"relative distance to the rule's boundary {dist[:8]}")
             boundary += int(bad.sum())
         scaled = blk32 * np.ldexp(1.0, -x_g)[:, None]
         ref_codes = F.fp8_quantize(F.round_nearest_even(scaled, F.FP32), fmt)

@@ -45,6 +45,7 @@ def test_enum_values_match_header():
                  "NORM_ERR_WORKSPACE_TOO_SMALL", "NORM_ERR_HIP", "NORM_LAYERNORM", "NORM_RMSNORM",
                  "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_FP8_E4M3", "NORM_FP8_E5M2",
                  "NORM_SCALING_NONE", "NORM_SCALING_DELAYED_TENSOR", "NORM_SCALING_MXFP8_1D32",
+                 "NORM_SCALING_MXFP8_1D32_CEIL",
                  "NORM_Q_ROWWISE", "NORM_Q_COLWISE", "NORM_Q_ROWWISE_COLWISE"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == getattr(L, name), name

@@ -223,6 +223,36 @@ def test_fwd_mxfp8(fp8, layout, norm, rows, hidden, zc):
     assert_ws_clean()
 
 
+@pytest.mark.parametrize("fp8", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("path", ["row", "tiles", "band"])
+@pytest.mark.parametrize("norm,rows,hidden", [("rmsnorm", 300, 4104), ("layernorm", 45, 1000),
+                                              ("rmsnorm", 130, 12288)])
+def test_fwd_mxfp8_round_up_rule(fp8, path, norm, rows, hidden):
+    """The round-up exponent rule on every forward path: rowwise only (row kernel), rowwise +
+    columnwise through the statistics pass + tiles, and the single-pass band kernel. No code
+    may saturate, and codes and bytes match the oracle under the same rule."""
+    case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=rows + 3 * hidden)
+    # spread the block maxima over many binades so that both rules' decisions vary
+    case["x"] = case["x"] * torch.exp(torch.linspace(-6.0, 6.0, rows))[:, None].to(case["x"].dtype)
+    ref = oracle_fwd(case, norm, "bf16", "f32", False)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    layout = "rowwise" if path == "row" else "rowwise_colwise"
+    with env(NORMFP8_COL_KERNEL=0 if path == "band" else 1):
+        out = nf.fwd(x, g, b, norm=norm, eps=EPS, scaling="mxfp8_ceil", fp8=fp8, layout=layout)
+    t = ln_terms(case, ref, norm)
+    checks.check_mx_rows(bits(out["y"]), bits(out["scale_inv"]), ref["v"], fp8, "mx rowwise", terms=t,
+                         rule="ceil")
+    if layout != "rowwise":
+        checks.check_mx_rows(bits(out["y_colwise"]), bits(out["colwise_scale_inv"]),
+                             np.ascontiguousarray(ref["v"].T), fp8, "mx colwise", terms=T(t), rule="ceil")
+    # the rules really differ on this input
+    fl = nf.fwd(x, g, b, norm=norm, eps=EPS, scaling="mxfp8", fp8=fp8, layout="rowwise")
+    assert int((bits(fl["scale_inv"]) != bits(out["scale_inv"])).sum()) > 0
+    checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
+                       out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+    assert_ws_clean()
+
+
 def test_fwd_mxfp8_zero_block():
     case = workloads.small_case("layernorm", 32, 256, "bf16", "f32", seed=4)
     case["gamma"][:32] = 0.0                          # first column block of every row is 0 * x + beta
