@@ -222,9 +222,10 @@ __global__ __launch_bounds__(64 * W * T) void bwd_kernel(BwdParams p) {
 
 // Fixed-order reduction of the G partials. Workgroup (x, y) owns column block x (32 columns)
 // of array y (0: dgamma, 1: dbeta), whose G partials are one contiguous [G][32] slab; thread
-// (c, q) adds 4 columns (one float4) of partials q, q + 32, q + 64, ... with four loads in
+// (c, q) adds 4 columns (one float4) of partials q, q + 32, q + 64, ... with eight loads in
 // flight (each load instruction reads 4 KB of the slab), and the 32 sums per column are added
-// in q order. The grid has ceil(H / 32) workgroups per array.
+// in a fixed order (groups of four q, then the eight groups). The grid has ceil(H / 32)
+// workgroups per array.
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(FinalizeParams p) {
   constexpr int Q = 32;
   const int c = threadIdx.x & 7;
@@ -235,34 +236,38 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(FinalizeParams p) {
   const float *part = p.part + which * arr + (int64_t)blockIdx.x * p.G * 32 + 4 * c;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (col < p.hidden) {
+    // eight loads in flight per thread (one round trip for G <= 256), added in g order
     int g = q;
-    for (; g + 3 * Q < p.G; g += 4 * Q) {
-      const float4 a = *reinterpret_cast<const float4 *>(part + (int64_t)g * 32);
-      const float4 b = *reinterpret_cast<const float4 *>(part + (int64_t)(g + Q) * 32);
-      const float4 e = *reinterpret_cast<const float4 *>(part + (int64_t)(g + 2 * Q) * 32);
-      const float4 f = *reinterpret_cast<const float4 *>(part + (int64_t)(g + 3 * Q) * 32);
-      s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
-      s.x += b.x; s.y += b.y; s.z += b.z; s.w += b.w;
-      s.x += e.x; s.y += e.y; s.z += e.z; s.w += e.w;
-      s.x += f.x; s.y += f.y; s.z += f.z; s.w += f.w;
+    for (; g + 7 * Q < p.G; g += 8 * Q) {
+      float4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const float4 *>(part + (int64_t)(g + j * Q) * 32);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
+      }
     }
     for (; g < p.G; g += Q) {
       const float4 a = *reinterpret_cast<const float4 *>(part + (int64_t)g * 32);
       s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
     }
   }
-  __shared__ float4 red[Q][8];
-  red[q][c] = s;
+  // the 32 sums of each column, in a fixed tree: eight groups of four q, then the groups
+  __shared__ __align__(16) float red[Q][32];
+  __shared__ float red2[8][32];
+  *reinterpret_cast<float4 *>(&red[q][4 * c]) = s;
+  __syncthreads();
+  {
+    const int j = threadIdx.x & 31, h = threadIdx.x >> 5;
+    red2[h][j] = ((red[4 * h][j] + red[4 * h + 1][j]) + red[4 * h + 2][j]) + red[4 * h + 3][j];
+  }
   __syncthreads();
   if (threadIdx.x < 32) {
-    const int cc = threadIdx.x >> 2, e = threadIdx.x & 3;
     const int64_t out = (int64_t)blockIdx.x * 32 + threadIdx.x;
     if (out < p.hidden) {
-      float t = 0.0f;
-      for (int w = 0; w < Q; ++w) {
-        const float4 v = red[w][cc];
-        t += e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
-      }
+      float t = red2[0][threadIdx.x];
+#pragma unroll
+      for (int h = 1; h < 8; ++h) t += red2[h][threadIdx.x];
       void *dst = which == 0 ? p.dgamma : p.dbeta;
       if (p.w_dtype == DT_F32) {
         static_cast<float *>(dst)[out] = t;
