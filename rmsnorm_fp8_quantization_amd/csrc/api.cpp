@@ -257,6 +257,13 @@ int plan_bwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_t
   if (cfg < 0)
     return fail(NORM_ERR_UNSUPPORTED, "backward supports hidden <= %lld in this build",
                 (long long)kBwdShapes[BWD_W16_K2].cover());
+  // with few rows per team (under four), one-team workgroups: the merge of the teams' partial
+  // sums would cost more than the smaller partial traffic saves
+  if (ov < 0 && rows < (int64_t)kMaxCus * kBwdShapes[cfg].T * 4) {
+    if (cfg == BWD_W2_K1) cfg = BWD_W2_K1_T1;
+    else if (cfg == BWD_W4_K1) cfg = BWD_W4_K1_T1;
+    else if (cfg == BWD_W4_K2) cfg = BWD_W4_K2_T1;
+  }
   pl->cfg = cfg;
   const int64_t gmax = (int64_t)kMaxCus * bwd_wgs_per_cu(cfg);
   pl->G_max = rows < gmax ? (rows > 0 ? rows : 1) : gmax;

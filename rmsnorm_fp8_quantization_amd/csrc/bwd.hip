@@ -297,6 +297,9 @@ static const void *pick_bwd_cfg(int cfg) {
     case BWD_W8_K1: return NF8_BWD(BWD_W8_K1);
     case BWD_W16_K1: return NF8_BWD(BWD_W16_K1);
     case BWD_W4_K4: return NF8_BWD(BWD_W4_K4);
+    case BWD_W2_K1_T1: return NF8_BWD(BWD_W2_K1_T1);
+    case BWD_W4_K1_T1: return NF8_BWD(BWD_W4_K1_T1);
+    case BWD_W4_K2_T1: return NF8_BWD(BWD_W4_K2_T1);
     default: return nullptr;
   }
 #undef NF8_BWD

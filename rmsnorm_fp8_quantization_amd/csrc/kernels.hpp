@@ -49,6 +49,9 @@ enum BwdCfg : int {
   BWD_W8_K1,
   BWD_W16_K1,
   BWD_W4_K4,
+  BWD_W2_K1_T1,  // one-team twins of the first three, for few rows per workgroup
+  BWD_W4_K1_T1,
+  BWD_W4_K2_T1,
   BWD_NCFG
 };
 // T teams of W waves per workgroup, each team on its own row; the teams share one partial
@@ -62,7 +65,8 @@ struct BwdShape {
 #define NF8_BWD_T4K2 2
 #endif
 constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1, 4}, {4, 1, 2}, {4, 2, NF8_BWD_T4K2}, {8, 2, 1},
-                                           {16, 2, 1}, {8, 1, 1}, {16, 1, 1}, {4, 4, 1}};
+                                           {16, 2, 1}, {8, 1, 1}, {16, 1, 1}, {4, 4, 1},
+                                           {2, 1, 1}, {4, 1, 1}, {4, 2, 1}};
 
 // ---- forward tile kernel (second pass of a columnwise output): 8 waves, 128 x 128 tiles
 constexpr int kColTileRows = 128;

@@ -112,7 +112,7 @@ def test_fwd_plain_other_out_dtype_and_bf16_weights(out_dt):
 
 
 ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096, 65536]   # per row layout
-BWD_COVER = [1024, 2048, 4096, 8192, 16384, 4096, 8192, 8192]
+BWD_COVER = [1024, 2048, 4096, 8192, 16384, 4096, 8192, 8192, 1024, 2048, 4096]
 
 
 @pytest.mark.parametrize("cfg", range(len(ROW_COVER)))
