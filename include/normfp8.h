@@ -76,7 +76,10 @@ typedef enum {
 typedef enum {
   NORM_Q_ROWWISE = 1,
   NORM_Q_COLWISE = 2,
-  NORM_Q_ROWWISE_COLWISE = 3
+  NORM_Q_ROWWISE_COLWISE = 3,
+  /* modifier, with NORM_Q_COLWISE: the columnwise output keeps the rowwise [rows, hidden] layout
+     (codes of the columnwise quantisation in place, MXFP8 scales [ceil(rows/32), hidden]) */
+  NORM_Q_COLWISE_ROWMAJOR = 4
 } norm_qlayout_t;
 
 /*
@@ -133,6 +136,10 @@ int norm_bwd_workspace_size(int64_t rows, int64_t hidden, int in_dtype, int w_dt
  *     smallest integer with amax_block * 2^-X <= the format's largest finite value (448 for
  *     E4M3, 57344 for E5M2), clamped to [-127, 127], so no code saturates. The pages leave the
  *     exponent rule of their MXFP8 mode open; the floor rule is the default reading.
+ *   With NORM_Q_COLWISE_ROWMAJOR added to a columnwise qlayout, y_colwise is [rows, hidden]
+ *     (element (r, c) holds the code the transposed layout keeps at (c, r)) and the MXFP8
+ *     colwise_scale_inv is uint8 [ceil(rows/32), hidden]; this build serves it for rows that a
+ *     row layout covers (hidden <= 65536) and returns NORM_ERR_UNSUPPORTED otherwise.
  *   The layout pointers not requested by qlayout must be NULL.
  *
  *   Errors: NORM_ERR_INVALID_ARG for NULL required pointers or bad codes; NORM_ERR_UNSUPPORTED

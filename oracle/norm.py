@@ -154,15 +154,23 @@ def mx_quantize_rows(v, fp8: str, block: int = 32, rule: str = "floor"):
     return codes, scales
 
 
-def mx_epilogue(v, fp8: str, colwise: bool, block: int = 32, rule: str = "floor"):
+def mx_epilogue(v, fp8: str, colwise: bool, block: int = 32, rule: str = "floor",
+                col_layout: str = "transposed"):
     """MXFP8 outputs: rowwise data [rows, hidden] + scales [rows, ceil(hidden/32)];
     colwise data [hidden, rows] + scales [hidden, ceil(rows/32)] (blocks of 32
-    consecutive rows of one column)."""
+    consecutive rows of one column). col_layout "rowmajor" returns the same columnwise codes
+    and scales in the rowwise orientation: data [rows, hidden], scales [ceil(rows/32), hidden]
+    (a layout choice only; the arithmetic is the transposed case's)."""
     out = {}
     out["rowwise"], out["rowwise_scale"] = mx_quantize_rows(v, fp8, block, rule)
     if colwise:
         vt = np.ascontiguousarray(np.asarray(v).T)
         out["colwise"], out["colwise_scale"] = mx_quantize_rows(vt, fp8, block, rule)
+        if col_layout == "rowmajor":
+            out["colwise"] = np.ascontiguousarray(out["colwise"].T)
+            out["colwise_scale"] = np.ascontiguousarray(out["colwise_scale"].T)
+        elif col_layout != "transposed":
+            raise ValueError(f"unknown columnwise layout {col_layout!r}")
     return out
 
 

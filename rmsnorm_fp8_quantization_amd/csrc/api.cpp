@@ -128,6 +128,7 @@ struct FwdPlan {
   size_t ws_bytes = 0;
   size_t partial_off = 0;
   size_t stats_off = 0;  // two-pass path: mu / rsigma when the caller passes none
+  bool col_rowmajor = false;
 };
 
 int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
@@ -138,6 +139,12 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   if (!is_hp(in_dtype)) return fail(NORM_ERR_UNSUPPORTED, "input dtype %d not supported", in_dtype);
   if (!is_hp(w_dtype)) return fail(NORM_ERR_UNSUPPORTED, "weight dtype %d not supported", w_dtype);
   if (cu_margin < 0) return fail(NORM_ERR_INVALID_ARG, "cu_margin must be >= 0");
+  const bool col_rowmajor = (qlayout & NORM_Q_COLWISE_ROWMAJOR) != 0;
+  if (col_rowmajor) {
+    if (!(qlayout & NORM_Q_COLWISE))
+      return fail(NORM_ERR_INVALID_ARG, "NORM_Q_COLWISE_ROWMAJOR modifies a columnwise layout");
+    qlayout &= ~NORM_Q_COLWISE_ROWMAJOR;
+  }
   if (qlayout < NORM_Q_ROWWISE || qlayout > NORM_Q_ROWWISE_COLWISE)
     return fail(NORM_ERR_INVALID_ARG, "unknown quantize layout %d", qlayout);
   if (hidden % 8 != 0) return fail(NORM_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 8", (long long)hidden);
@@ -181,6 +188,10 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   const bool tile_fits = (int64_t)hidden * 4 * kColTileRows < (1ll << 32) && rows * kColTileCols < (1ll << 32);
   pl->col = pl->colwise && row_cfg >= 0 && tile_fits && !force_band && env_int("NORMFP8_COL_KERNEL", 1) != 0;
   pl->band = !pl->col && (pl->colwise || row_cfg < 0 || force_band);
+  pl->col_rowmajor = col_rowmajor;
+  if (col_rowmajor && !pl->col)
+    return fail(NORM_ERR_UNSUPPORTED, "the row-major columnwise layout needs rows a row layout covers "
+                                      "(hidden <= 65536) and the tile path");
   if (!pl->band) {
     pl->cfg = row_cfg;
   } else {
@@ -428,7 +439,8 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     tp.tiles_r = cdiv(rows, kColTileRows);
     tp.tiles_c = cdiv(hidden, kColTileCols);
     tp.write_row = pl.rowwise ? 1 : 0;
-    const void *fn = fwd_tile_kernel_ptr(norm_type, in_dtype, pl.mode);
+    tp.col_rowmajor = pl.col_rowmajor ? 1 : 0;
+    const void *fn = fwd_tile_kernel_ptr(norm_type, in_dtype, pl.mode, pl.col_rowmajor);
     if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no forward tile kernel for this combination");
     int occ = 1;
     rc = occupancy(fn, kColThreads, &occ);

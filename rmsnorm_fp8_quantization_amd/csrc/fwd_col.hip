@@ -8,6 +8,9 @@
 // columnwise tensor is [hidden, rows] (the transpose), and for MXFP8 each columnwise block is
 // 32 consecutive rows of one column.
 //
+// With CRM (col_rowmajor) the columnwise codes keep the rowwise [rows, hidden] layout (no transpose)
+// and the MXFP8 columnwise scales are [ceil(rows/32), hidden].
+//
 // Two passes: the row kernel first writes mu / rsigma of every row (MODE_STATS); this kernel
 // then works on independent tiles. A column of the transposed output is contiguous along
 // rows and column pieces shorter than a 128-byte line are not merged on their way to HBM, so
@@ -63,7 +66,7 @@ __device__ __forceinline__ float rowgroup_max(float v) {
 
 }  // namespace
 
-template <int NORM, class IN, int MODE>
+template <int NORM, class IN, int MODE, bool CRM>
 __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp) {
   static_assert(MODE == MODE_DELAYED || MODE == MODE_MX, "columnwise output is FP8");
   static_assert(kColThreads == 512, "8 waves of 16 rows");
@@ -266,7 +269,13 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
         codes[k] = fp8_pack8(u, fmt);
       }
     }
-    {
+    if constexpr (CRM) {
+      // columnwise codes in the rowwise layout: stored like the rowwise codes
+      uint8_t *const ycr = static_cast<uint8_t *>(tp.y_col) + T.r0 * H + T.c0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k < valid && cv) st_nt8(ycr + (size_t)((uint32_t)(rloc + k) * Hu + (uint32_t)cloc), codes[k]);
+    } else {
       uint32_t lo[4], hi[4];  // lo[i]: column i, hi[i]: column 4 + i; byte k = row k
       transpose4x4b(codes[0].x, codes[1].x, codes[2].x, codes[3].x, lo);
       transpose4x4b(codes[0].y, codes[1].y, codes[2].y, codes[3].y, hi);
@@ -282,7 +291,7 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
     uint8_t *const yct = static_cast<uint8_t *>(tp.y_col) + T.c0 * N + T.r0;
     const int m = tid & 7;
 #pragma unroll
-    for (int pass = 0; pass < kTC / 64; ++pass) {
+    for (int pass = 0; pass < (CRM ? 0 : kTC / 64); ++pass) {
       const int c = pass * 64 + (tid >> 3);
       if (c < T.cols_here) {
         const uint4 v = *reinterpret_cast<const uint4 *>(stg + stage_off(c, 4 * m));
@@ -300,10 +309,15 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
     if constexpr (MODE == MODE_MX) {
       // the tile's (up to) four 32-row block exponents of each column, consecutive bytes
       if (tid < T.cols_here) {
-        uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + T.c0 * tp.mx_rows + 4 * (int64_t)T.rt +
-                       (size_t)((uint32_t)tid * (uint32_t)tp.mx_rows);
         const int nb = (T.rows_here + 31) / 32;
-        for (int q = 0; q < nb; ++q) dst[q] = colx[q][tid];
+        if constexpr (CRM) {  // [ceil(rows/32), hidden]: one 128-byte run per block row
+          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + 4 * (int64_t)T.rt * H + T.c0 + tid;
+          for (int q = 0; q < nb; ++q) dst[(size_t)q * Hu] = colx[q][tid];
+        } else {
+          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + T.c0 * tp.mx_rows + 4 * (int64_t)T.rt +
+                         (size_t)((uint32_t)tid * (uint32_t)tp.mx_rows);
+          for (int q = 0; q < nb; ++q) dst[q] = colx[q][tid];
+        }
       }
     }
     // No barrier here: the next tile stages into the other buffer, and it rewrites cmax /
@@ -346,26 +360,31 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
 }
 
 template <int NORM, class IN>
-static const void *pick_tile_mode(int mode) {
+static const void *pick_tile_mode(int mode, bool crm) {
   switch (mode) {
-    case MODE_DELAYED: return (const void *)fwd_tile_kernel<NORM, IN, MODE_DELAYED>;
-    case MODE_MX: return (const void *)fwd_tile_kernel<NORM, IN, MODE_MX>;
+    case MODE_DELAYED:
+      return crm ? (const void *)fwd_tile_kernel<NORM, IN, MODE_DELAYED, true>
+                 : (const void *)fwd_tile_kernel<NORM, IN, MODE_DELAYED, false>;
+    case MODE_MX:
+      return crm ? (const void *)fwd_tile_kernel<NORM, IN, MODE_MX, true>
+                 : (const void *)fwd_tile_kernel<NORM, IN, MODE_MX, false>;
     default: return nullptr;
   }
 }
 
 template <int NORM>
-static const void *pick_tile_in(int in_dtype, int mode) {
+static const void *pick_tile_in(int in_dtype, int mode, bool crm) {
   switch (in_dtype) {
-    case DT_F32: return pick_tile_mode<NORM, F32>(mode);
-    case DT_BF16: return pick_tile_mode<NORM, BF16>(mode);
-    case DT_F16: return pick_tile_mode<NORM, F16>(mode);
+    case DT_F32: return pick_tile_mode<NORM, F32>(mode, crm);
+    case DT_BF16: return pick_tile_mode<NORM, BF16>(mode, crm);
+    case DT_F16: return pick_tile_mode<NORM, F16>(mode, crm);
     default: return nullptr;
   }
 }
 
-const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode) {
-  return norm == NT_LAYERNORM ? pick_tile_in<NT_LAYERNORM>(in_dtype, mode) : pick_tile_in<NT_RMSNORM>(in_dtype, mode);
+const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor) {
+  return norm == NT_LAYERNORM ? pick_tile_in<NT_LAYERNORM>(in_dtype, mode, col_rowmajor)
+                              : pick_tile_in<NT_RMSNORM>(in_dtype, mode, col_rowmajor);
 }
 
 }  // namespace nf8

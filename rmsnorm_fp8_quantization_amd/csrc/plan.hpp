@@ -103,6 +103,7 @@ struct FwdTileParams {
   int64_t tiles_r;       // ceil(rows / 128)
   int64_t tiles_c;       // ceil(hidden / 128)
   int write_row;         // rowwise output requested
+  int col_rowmajor;      // columnwise output in the [rows, hidden] layout (scales [rows/32, hidden])
 };
 
 // ---- backward ------------------------------------------------------------------------------

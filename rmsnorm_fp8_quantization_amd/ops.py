@@ -26,7 +26,10 @@ _NORM = {"layernorm": L.NORM_LAYERNORM, "rmsnorm": L.NORM_RMSNORM}
 _SCALING = {"none": L.NORM_SCALING_NONE, "delayed": L.NORM_SCALING_DELAYED_TENSOR,
             "mxfp8": L.NORM_SCALING_MXFP8_1D32, "mxfp8_ceil": L.NORM_SCALING_MXFP8_1D32_CEIL}
 _LAYOUT = {"rowwise": L.NORM_Q_ROWWISE, "colwise": L.NORM_Q_COLWISE,
-           "rowwise_colwise": L.NORM_Q_ROWWISE_COLWISE}
+           "rowwise_colwise": L.NORM_Q_ROWWISE_COLWISE,
+           # columnwise output kept in the [rows, hidden] layout
+           "colwise_rowmajor": L.NORM_Q_COLWISE | L.NORM_Q_COLWISE_ROWMAJOR,
+           "rowwise_colwise_rowmajor": L.NORM_Q_ROWWISE_COLWISE | L.NORM_Q_COLWISE_ROWMAJOR}
 
 _ws_cache: Dict[tuple, torch.Tensor] = {}
 
@@ -108,8 +111,9 @@ def prepare_fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tenso
         raise ValueError("x must be [rows, hidden]")
     rows, hidden = x.shape
     dev = x.device
-    rowwise = layout in ("rowwise", "rowwise_colwise")
-    colwise = layout in ("colwise", "rowwise_colwise")
+    rowwise = layout in ("rowwise", "rowwise_colwise", "rowwise_colwise_rowmajor")
+    colwise = layout != "rowwise"
+    col_rowmajor = layout.endswith("_rowmajor")
     if scaling == "none":
         odt = out_dtype or x.dtype
         out_code = _DT[odt]
@@ -117,7 +121,8 @@ def prepare_fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tenso
     else:
         out_code = _FP8[fp8]
         y = torch.empty(rows, hidden, dtype=torch.uint8, device=dev) if rowwise else None
-    y_col = torch.empty(hidden, rows, dtype=torch.uint8, device=dev) if colwise else None
+    y_col = (torch.empty(*((rows, hidden) if col_rowmajor else (hidden, rows)), dtype=torch.uint8, device=dev)
+             if colwise else None)
     mu = torch.empty(rows, dtype=torch.float32, device=dev) if norm == "layernorm" else None
     rs = torch.empty(rows, dtype=torch.float32, device=dev)
     si = csi = upd = None
@@ -129,7 +134,8 @@ def prepare_fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tenso
         upd = amax if amax_inplace else torch.empty(1, dtype=torch.float32, device=dev)
     elif scaling in ("mxfp8", "mxfp8_ceil"):
         si = torch.empty(rows, (hidden + 31) // 32, dtype=torch.uint8, device=dev) if rowwise else None
-        csi = torch.empty(hidden, (rows + 31) // 32, dtype=torch.uint8, device=dev) if colwise else None
+        csi_shape = ((rows + 31) // 32, hidden) if col_rowmajor else (hidden, (rows + 31) // 32)
+        csi = torch.empty(*csi_shape, dtype=torch.uint8, device=dev) if colwise else None
     nbytes = fwd_workspace_size(rows, hidden, x.dtype, gamma.dtype, out_code, norm, scaling, layout,
                                 zero_centered_gamma, eps, cu_margin, training)
     ws = workspace(nbytes, dev) if nbytes else None
@@ -152,7 +158,9 @@ def fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor] = Non
     "rmsnorm"), eps, zero_centered_gamma, scaling ("none" | "delayed" | "mxfp8" | "mxfp8_ceil": MXFP8 with the round-up exponent
     rule, no saturation), out_dtype
     (scaling "none"), fp8 ("e4m3" | "e5m2"), scale / amax (float32[1] GPU tensors, delayed
-    scaling), layout ("rowwise" | "colwise" | "rowwise_colwise"), cu_margin, amax_inplace.
+    scaling), layout ("rowwise" | "colwise" | "rowwise_colwise", or "colwise_rowmajor" /
+    "rowwise_colwise_rowmajor" for a columnwise output kept in the [rows, hidden] layout, with MXFP8
+    columnwise scales [ceil(rows/32), hidden]), cu_margin, amax_inplace.
     Returns ``y`` (rowwise output: out_dtype, or uint8 FP8 codes), ``y_colwise`` ([hidden, rows]
     uint8 codes), ``mu`` (LayerNorm), ``rsigma``, ``scale_inv`` / ``colwise_scale_inv``
     (float32[1] for delayed scaling, uint8 E8M0 grids for MXFP8) and ``amax`` (updated amax)."""

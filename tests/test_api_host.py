@@ -46,7 +46,7 @@ def test_enum_values_match_header():
                  "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_FP8_E4M3", "NORM_FP8_E5M2",
                  "NORM_SCALING_NONE", "NORM_SCALING_DELAYED_TENSOR", "NORM_SCALING_MXFP8_1D32",
                  "NORM_SCALING_MXFP8_1D32_CEIL",
-                 "NORM_Q_ROWWISE", "NORM_Q_COLWISE", "NORM_Q_ROWWISE_COLWISE"):
+                 "NORM_Q_ROWWISE", "NORM_Q_COLWISE", "NORM_Q_ROWWISE_COLWISE", "NORM_Q_COLWISE_ROWMAJOR"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == getattr(L, name), name
     m = re.search(r"#define NORM_WS_HEADER_BYTES (\d+)", src)
@@ -207,3 +207,17 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         mod.load()
+
+
+def test_colwise_rowmajor_layout_validation(monkeypatch):
+    mx = dict(out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_MXFP8_1D32)
+    rm = L.NORM_Q_COLWISE | L.NORM_Q_COLWISE_ROWMAJOR
+    assert fwd_ws(64, 1024, layout=rm, **mx)[0] == L.NORM_OK
+    assert fwd_ws(64, 1024, layout=L.NORM_Q_ROWWISE_COLWISE | L.NORM_Q_COLWISE_ROWMAJOR, **mx)[0] == L.NORM_OK
+    # the modifier alone, or with a rowwise-only layout, is not a layout
+    assert fwd_ws(64, 1024, layout=L.NORM_Q_COLWISE_ROWMAJOR, **mx)[0] == L.NORM_ERR_INVALID_ARG
+    assert fwd_ws(64, 1024, layout=L.NORM_Q_ROWWISE | L.NORM_Q_COLWISE_ROWMAJOR, **mx)[0] == L.NORM_ERR_INVALID_ARG
+    # served by the tile path only: rows longer than the row layouts, or the band kernel forced
+    assert fwd_ws(16, 131072, layout=rm, **mx)[0] == L.NORM_ERR_UNSUPPORTED
+    monkeypatch.setenv("NORMFP8_COL_KERNEL", "0")
+    assert fwd_ws(64, 1024, layout=rm, **mx)[0] == L.NORM_ERR_UNSUPPORTED

@@ -301,6 +301,45 @@ def test_fwd_colwise_tiles(scaling, norm, rows, hidden):
     assert_ws_clean()
 
 
+@pytest.mark.parametrize("scaling", ["delayed", "mxfp8", "mxfp8_ceil"])
+@pytest.mark.parametrize("layout", ["colwise_rowmajor", "rowwise_colwise_rowmajor"])
+@pytest.mark.parametrize("norm,rows,hidden", [("rmsnorm", 300, 4104), ("layernorm", 45, 1000),
+                                              ("rmsnorm", 256, 8192)])
+def test_fwd_colwise_rowmajor(scaling, layout, norm, rows, hidden):
+    """The columnwise output in the rowwise [rows, hidden] orientation: bitwise the transpose of
+    the transposed layout's output on the same inputs, and against the oracle."""
+    case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=rows + hidden + 1)
+    ref = oracle_fwd(case, norm, "bf16", "f32", False)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    kw = dict(norm=norm, eps=EPS)
+    if scaling == "delayed":
+        scale = float(np.float32(448.0) / np.float32(np.max(np.abs(ref["v"]))))
+        kw.update(scaling="delayed", scale=torch.tensor([scale], device="cuda"))
+    else:
+        kw.update(scaling=scaling)
+    fresh = (lambda: dict(amax=torch.zeros(1, device="cuda"))) if scaling == "delayed" else dict
+    out = nf.fwd(x, g, b, layout=layout, **kw, **fresh())
+    tr = nf.fwd(x, g, b, layout=layout.replace("_rowmajor", ""), **kw, **fresh())
+    assert out["y_colwise"].shape == (rows, hidden)
+    assert torch.equal(out["y_colwise"], tr["y_colwise"].T)
+    if layout.startswith("rowwise"):
+        assert torch.equal(out["y"], tr["y"])
+    t = ln_terms(case, ref, norm)
+    if scaling == "delayed":
+        assert torch.equal(out["colwise_scale_inv"], tr["colwise_scale_inv"])
+        got = {"y": None, "y_colwise": np.ascontiguousarray(bits(out["y_colwise"]).T), "scale_inv": None,
+               "colwise_scale_inv": out["colwise_scale_inv"].item(), "amax": out["amax"].item()}
+        checks.check_delayed(got, ref["v"], scale, 0.0, "e4m3", rowwise=False, colwise=True, terms=t)
+    else:
+        assert out["colwise_scale_inv"].shape == ((rows + 31) // 32, hidden)
+        assert torch.equal(out["colwise_scale_inv"], tr["colwise_scale_inv"].T)
+        checks.check_mx_rows(np.ascontiguousarray(bits(out["y_colwise"]).T),
+                             np.ascontiguousarray(bits(out["colwise_scale_inv"]).T),
+                             np.ascontiguousarray(ref["v"].T), "e4m3", "mx colwise", terms=T(t),
+                             rule="ceil" if scaling == "mxfp8_ceil" else "floor")
+    assert_ws_clean()
+
+
 @pytest.mark.parametrize("in_dt", ["f32", "f16"])
 @pytest.mark.parametrize("layout", ["colwise", "rowwise_colwise"])
 def test_fwd_colwise_other_input_dtypes(in_dt, layout):

@@ -207,6 +207,27 @@ def test_mx_zero_block_and_colwise_layout():
     assert r5 == math.floor(math.log2(5.0)) - 8 + 127
 
 
+def test_mx_colwise_rowmajor_bruteforce_small():
+    """The columnwise output in the rowwise orientation, worked element by element along the
+    columns of a small matrix (70 rows: the last block of each column has 6 rows)."""
+    v = _rand((70, 3), 18) * np.exp(_rand((70, 3), 19))
+    out = N.mx_epilogue(v, "e4m3", colwise=True, col_layout="rowmajor")
+    codes, scales = out["colwise"], out["colwise_scale"]
+    assert codes.shape == (70, 3) and scales.shape == (3, 3)
+    table = F.fp8_decode(np.arange(256), F.E4M3)
+    fin = [c for c in range(256) if math.isfinite(table[c])]
+    for j in range(3):
+        for b in range(3):
+            blk = [float(np.float32(t)) for t in v[32 * b:32 * b + 32, j]]
+            a = max(abs(t) for t in blk)
+            x = math.floor(math.log2(a)) - 8
+            assert scales[b, j] == x + 127
+            for i, t in enumerate(blk):
+                u = max(-448.0, min(448.0, t * 2.0 ** (-x)))
+                best = min(fin, key=lambda k: (abs(table[k] - u), k % 2, k))
+                assert table[codes[32 * b + i, j]] == table[best]
+
+
 # ------------------------------------------------------------------- backward
 
 def _loss(x, gamma, beta, dy, norm, eps):
