@@ -16,8 +16,12 @@
  *    enqueued on that stream only. The library never synchronises, never allocates or frees
  *    device memory and never reads device memory on the host (norm_workspace_check excepted).
  *  - Tensors are device pointers to dense row-major storage. x-like tensors are [rows, hidden]
- *    with row stride `hidden`. Pointers must be 16-byte aligned; `hidden` must be a multiple
- *    of 8. The caller owns every buffer, including the workspace.
+ *    with row stride `hidden` (1 <= hidden <= 2^24). Tensor pointers must be aligned to their
+ *    element size and the workspace to 16 bytes. The vector kernels serve 16-byte-aligned
+ *    tensors with hidden a multiple of 8 (rows up to 16384 elements in the backward); any other
+ *    case goes to the general kernels ([NVRTC-PR] Greptile Summary: general variants beside the
+ *    tuned ones), which compute the same results element by element, more slowly. The caller
+ *    owns every buffer, including the workspace.
  *  - Element types are given by norm_dtype_t codes. Statistics (mu, rsigma) and the amax /
  *    scale / scale_inv scalars are always float32. rows == 0 is valid: row-indexed buffers
  *    (x, y, y_colwise, dy, dx, residual_dy, mu, rsigma, MXFP8 scale grids) may then be NULL;
@@ -47,7 +51,7 @@ typedef enum {
   NORM_OK = 0,
   NORM_ERR_INVALID_ARG = 1,         /* NULL where a pointer is required, bad enum, negative size */
   NORM_ERR_UNSUPPORTED = 2,         /* valid request outside what this build implements */
-  NORM_ERR_MISALIGNED = 3,          /* pointer not 16-byte aligned */
+  NORM_ERR_MISALIGNED = 3,          /* pointer not aligned to its element size (workspace: 16 bytes) */
   NORM_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes below the query's answer */
   NORM_ERR_HIP = 5                  /* a HIP runtime call failed (message has hipGetErrorString) */
 } norm_status_t;

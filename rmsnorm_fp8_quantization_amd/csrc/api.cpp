@@ -129,6 +129,7 @@ struct FwdPlan {
   size_t partial_off = 0;
   size_t stats_off = 0;  // two-pass path: mu / rsigma when the caller passes none
   bool col_rowmajor = false;
+  bool gen = false;   // general kernels: hidden not a multiple of 8 (or, at launch, unaligned tensors)
 };
 
 int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
@@ -147,8 +148,8 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   }
   if (qlayout < NORM_Q_ROWWISE || qlayout > NORM_Q_ROWWISE_COLWISE)
     return fail(NORM_ERR_INVALID_ARG, "unknown quantize layout %d", qlayout);
-  if (hidden % 8 != 0) return fail(NORM_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 8", (long long)hidden);
   if (hidden > (int64_t)1 << 24) return fail(NORM_ERR_UNSUPPORTED, "hidden above 2^24 not supported");
+  pl->gen = hidden % 8 != 0;
   switch (scaling) {
     case NORM_SCALING_NONE:
       if (!is_hp(out_dtype)) return fail(NORM_ERR_UNSUPPORTED, "no-scaling output must be F32/F16/BF16");
@@ -189,10 +190,15 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   pl->col = pl->colwise && row_cfg >= 0 && tile_fits && !force_band && env_int("NORMFP8_COL_KERNEL", 1) != 0;
   pl->band = !pl->col && (pl->colwise || row_cfg < 0 || force_band);
   pl->col_rowmajor = col_rowmajor;
-  if (col_rowmajor && !pl->col)
+  if (pl->gen) {  // the general kernels: rows, then (columnwise) the column pass
+    pl->col = pl->band = false;
+  } else if (col_rowmajor && !pl->col) {
     return fail(NORM_ERR_UNSUPPORTED, "the row-major columnwise layout needs rows a row layout covers "
                                       "(hidden <= 65536) and the tile path");
-  if (!pl->band) {
+  }
+  if (pl->gen) {
+    // no layout to choose
+  } else if (!pl->band) {
     pl->cfg = row_cfg;
   } else {
     int bc;
@@ -220,7 +226,9 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     const int nv = norm_type == NORM_LAYERNORM ? 2 : 1;
     ws += round_up((size_t)pl->bands * pl->S * pl->tile_rows * nv * sizeof(uint64_t), 256);
   }
-  if (pl->col) {
+  // row statistics of a columnwise request (two-pass paths; sized for every columnwise request,
+  // since unaligned tensors send any request to the general kernels at launch)
+  if (pl->colwise) {
     pl->stats_off = ws;
     ws += round_up((size_t)rows * sizeof(float) * (norm_type == NORM_LAYERNORM ? 2 : 1), 256);
   }
@@ -235,7 +243,9 @@ struct BwdPlan {
   int cfg = 0;
   int64_t G_max = 0;  // partial rows the workspace holds
   size_t ws_bytes = 0;
+  bool gen = false;   // general kernels (hidden not a multiple of 8, or beyond the row layouts)
 };
+constexpr int kGenChunks = 256;  // most row chunks (weight-gradient partials) of the general backward
 
 constexpr int kMaxCus = 256;  // gfx950 (MI355X) compute units; bounds the workspace query
 
@@ -252,7 +262,7 @@ int plan_bwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_t
   if (!is_hp(in_dtype)) return fail(NORM_ERR_UNSUPPORTED, "input dtype %d not supported", in_dtype);
   if (!is_hp(w_dtype)) return fail(NORM_ERR_UNSUPPORTED, "weight dtype %d not supported", w_dtype);
   if (cu_margin < 0) return fail(NORM_ERR_INVALID_ARG, "cu_margin must be >= 0");
-  if (hidden % 8 != 0) return fail(NORM_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 8", (long long)hidden);
+  if (hidden > (int64_t)1 << 24) return fail(NORM_ERR_UNSUPPORTED, "hidden above 2^24 not supported");
   int cfg = -1;
   const int ov = env_int("NORMFP8_BWD_CFG", -1);
   if (ov >= 0 && ov < BWD_NCFG && kBwdShapes[ov].cover() >= hidden) {
@@ -265,9 +275,14 @@ int plan_bwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_t
         break;
       }
   }
-  if (cfg < 0)
-    return fail(NORM_ERR_UNSUPPORTED, "backward supports hidden <= %lld in this build",
-                (long long)kBwdShapes[BWD_W16_K2].cover());
+  const int arrays = norm_type == NORM_LAYERNORM ? 2 : 1;
+  if (cfg < 0 || hidden % 8 != 0) {  // the general kernels
+    pl->gen = true;
+    pl->cfg = -1;
+    pl->G_max = kGenChunks;
+    pl->ws_bytes = kWsHeaderBytes + round_up((size_t)pl->G_max * round_up((size_t)hidden, 32) * arrays * sizeof(float), 256);
+    return NORM_OK;
+  }
   // with few rows per team (under four), one-team workgroups: the merge of the teams' partial
   // sums would cost more than the smaller partial traffic saves
   if (ov < 0 && rows < (int64_t)kMaxCus * kBwdShapes[cfg].T * 4) {
@@ -278,10 +293,14 @@ int plan_bwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_t
   pl->cfg = cfg;
   const int64_t gmax = (int64_t)kMaxCus * bwd_wgs_per_cu(cfg);
   pl->G_max = rows < gmax ? (rows > 0 ? rows : 1) : gmax;
-  const int arrays = norm_type == NORM_LAYERNORM ? 2 : 1;
+  // (a launch with unaligned tensors takes the general kernels, whose partials fit as well)
+  if (pl->G_max < kGenChunks) pl->G_max = kGenChunks;
   pl->ws_bytes = kWsHeaderBytes + round_up((size_t)pl->G_max * round_up((size_t)hidden, 32) * arrays * sizeof(float), 256);
   return NORM_OK;
 }
+
+bool aligned_to(const void *p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+size_t elem_bytes(int dt) { return dt == DT_F32 ? 4 : (is_hp(dt) ? 2 : 1); }
 
 int check_ws(void *ws, size_t have, size_t need) {
   if (need == 0) return NORM_OK;
@@ -356,8 +375,23 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
       return fail(NORM_ERR_INVALID_ARG, "colwise_scale_inv is required for columnwise output");
   }
   if (!(epsilon >= 0.0f)) return fail(NORM_ERR_INVALID_ARG, "epsilon must be >= 0");
-  for (const void *ptr : {x, gamma, beta, (const void *)y, (const void *)y_colwise})
-    if (ptr && !aligned16(ptr)) return fail(NORM_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+  // tensors must be aligned to their element size; the vector kernels need 16 bytes, anything
+  // less goes to the general kernels
+  {
+    const void *ptrs[] = {x, gamma, beta, y, y_colwise, mu, rsigma};
+    const size_t sizes[] = {elem_bytes(in_dtype), elem_bytes(w_dtype), elem_bytes(w_dtype), elem_bytes(out_dtype),
+                            1, 4, 4};
+    for (int i = 0; i < 7; ++i) {
+      if (!ptrs[i]) continue;
+      if (!aligned_to(ptrs[i], sizes[i]))
+        return fail(NORM_ERR_MISALIGNED, "tensor pointers must be aligned to their element size");
+      if (i < 5 && !aligned16(ptrs[i])) pl.gen = true;
+    }
+    if (pl.mode == MODE_DELAYED)
+      for (const void *q : {(const void *)scale, (const void *)amax, (const void *)updated_amax, (const void *)scale_inv,
+                            (const void *)colwise_scale_inv})
+        if (q && !aligned_to(q, 4)) return fail(NORM_ERR_MISALIGNED, "float32 scalars must be 4-byte aligned");
+  }
   rc = check_ws(workspace, workspace_bytes, pl.ws_bytes);
   if (rc) return rc;
 
@@ -365,10 +399,10 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   if (rows == 0) {
     if (pl.mode != MODE_DELAYED) return ok();  // nothing to compute
     // delayed scaling still publishes updated_amax = amax and scale_inv = 1/scale: one
-    // workgroup of the row kernel does that without visiting any row
+    // workgroup of the (general) row kernel does that without visiting any row
     pl.band = false;
     pl.col = false;
-    pl.cfg = ROW_W1_K1;
+    pl.gen = true;
   }
 
   DeviceInfo dev;
@@ -412,6 +446,52 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     FwdRowParams copy = rp;
     return launch(fn, dim3((unsigned)grid), dim3(sh.threads()), &copy, st);
   };
+  if (pl.gen) {
+    // rows (statistics and rowwise output; delayed scaling's amax), then the column pass
+    float *st_mu = nullptr, *st_rs = rsigma;
+    if (pl.colwise) {
+      if (!st_rs) st_rs = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.stats_off);
+      if (ln) st_mu = mu ? mu : reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.stats_off) + rows;
+    }
+    FwdRowParams r = f;
+    r.mu = ln ? (pl.colwise ? st_mu : mu) : nullptr;
+    r.rsigma = st_rs;
+    int mode1 = pl.mode;
+    if (!pl.rowwise) {
+      r.y = nullptr;
+      r.scale_inv = nullptr;
+      if (mode1 == MODE_MX) mode1 = MODE_STATS;
+    }
+    const void *fn = fwd_gen_row_kernel_ptr(norm_type, in_dtype, mode1);
+    if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no general forward kernel for this combination");
+    int occ = 1;
+    rc = occupancy(fn, 256, &occ);
+    if (rc) return rc;
+    int64_t grid = cdiv(rows, 4);
+    int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
+    if (cap > kMaxGrid) cap = kMaxGrid;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    rc = launch(fn, dim3((unsigned)grid), dim3(256), &r, st);
+    if (rc) return rc;
+    if (pl.colwise && (rows > 0 || pl.mode == MODE_DELAYED)) {  // (delayed: colwise_scale_inv too)
+      FwdTileParams tp{};
+      tp.f = f;
+      tp.y_col = y_colwise;
+      tp.col_scale_inv = colwise_scale_inv;
+      tp.st_mu = st_mu;
+      tp.st_rs = st_rs;
+      tp.mx_rows = cdiv(rows, 32);
+      tp.col_rowmajor = pl.col_rowmajor ? 1 : 0;
+      const void *fc = fwd_gen_col_kernel_ptr(norm_type, in_dtype, pl.mode, pl.col_rowmajor);
+      if (!fc) return fail(NORM_ERR_UNSUPPORTED, "no general columnwise kernel for this combination");
+      const int64_t items = cdiv(hidden, 64) * tp.mx_rows;
+      const int64_t g2 = items < 1 ? 1 : (items < (1 << 20) ? items : (1 << 20));
+      rc = launch(fc, dim3((unsigned)g2), dim3(64), &tp, st);
+      if (rc) return rc;
+    }
+    return ok();
+  }
   if (!pl.band && !pl.col) {
     rc = launch_rows(f, pl.mode);
     if (rc) return rc;
@@ -503,8 +583,17 @@ static int bwd_common(void *stream, bool with_add, const void *dy, const void *x
     return fail(NORM_ERR_INVALID_ARG, "dy, x, rsigma, gamma, dx and dgamma are required");
   if (ln && ((any && !mu) || !dbeta)) return fail(NORM_ERR_INVALID_ARG, "LayerNorm backward needs mu and dbeta");
   if (!ln && dbeta) return fail(NORM_ERR_INVALID_ARG, "dbeta must be NULL for RMSNorm");
-  for (const void *ptr : {dy, x, residual, gamma, (const void *)dx, (const void *)dgamma, (const void *)dbeta})
-    if (ptr && !aligned16(ptr)) return fail(NORM_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+  {
+    const void *ptrs[] = {dy, x, residual, dx, gamma, dgamma, dbeta, mu, rsigma};
+    const size_t sizes[] = {elem_bytes(in_dtype), elem_bytes(in_dtype), elem_bytes(in_dtype), elem_bytes(in_dtype),
+                            elem_bytes(w_dtype), elem_bytes(w_dtype), elem_bytes(w_dtype), 4, 4};
+    for (int i = 0; i < 9; ++i) {
+      if (!ptrs[i]) continue;
+      if (!aligned_to(ptrs[i], sizes[i]))
+        return fail(NORM_ERR_MISALIGNED, "tensor pointers must be aligned to their element size");
+      if (i < 5 && !aligned16(ptrs[i])) pl.gen = true;  // the vector kernels need 16 bytes
+    }
+  }
   rc = check_ws(workspace, workspace_bytes, pl.ws_bytes);
   if (rc) return rc;
 
@@ -513,6 +602,55 @@ static int bwd_common(void *stream, bool with_add, const void *dy, const void *x
   if (rc) return rc;
   if (cu_margin >= dev.cus) return fail(NORM_ERR_INVALID_ARG, "cu_margin (%d) >= CU count (%d)", cu_margin, dev.cus);
   hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (pl.gen) {
+    // dx one wave per row, then the weight-gradient partials of row chunks, then the finalize
+    BwdParams p{};
+    p.dy = dy;
+    p.x = x;
+    p.residual = residual;
+    p.mu = ln ? mu : nullptr;
+    p.rsigma = rsigma;
+    p.gamma = gamma;
+    p.dx = dx;
+    p.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + kWsHeaderBytes);
+    p.rows = rows;
+    p.hidden = hidden;
+    p.w_dtype = w_dtype;
+    p.zero_centered = zero_centered_gamma ? 1 : 0;
+    int64_t G = rows / 16;
+    if (G > kGenChunks) G = kGenChunks;
+    if (G < 1) G = 1;
+    p.G = (int)G;
+    if (rows > 0) {
+      const void *fr = bwd_gen_row_kernel_ptr(norm_type, in_dtype, with_add);
+      if (!fr) return fail(NORM_ERR_UNSUPPORTED, "no general backward kernel for this combination");
+      int occ = 1;
+      rc = occupancy(fr, 256, &occ);
+      if (rc) return rc;
+      int64_t grid = cdiv(rows, 4);
+      const int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
+      if (grid > cap) grid = cap;
+      if (grid < 1) grid = 1;
+      rc = launch(fr, dim3((unsigned)grid), dim3(256), &p, st);
+      if (rc) return rc;
+    }
+    const void *fw = bwd_gen_wgrad_kernel_ptr(norm_type, in_dtype);
+    if (!fw) return fail(NORM_ERR_UNSUPPORTED, "no general weight-gradient kernel for this combination");
+    const int64_t items = cdiv(hidden, 64) * G;
+    rc = launch(fw, dim3((unsigned)(items < (1 << 20) ? items : (1 << 20))), dim3(64), &p, st);
+    if (rc) return rc;
+    FinalizeParams fp{};
+    fp.part = p.part;
+    fp.dgamma = dgamma;
+    fp.dbeta = ln ? dbeta : nullptr;
+    fp.hidden = hidden;
+    fp.G = (int)G;
+    fp.w_dtype = w_dtype;
+    rc = launch(bwd_finalize_kernel_ptr(), dim3((unsigned)cdiv(hidden, 32), ln ? 2 : 1), dim3(256), &fp, st);
+    if (rc) return rc;
+    return ok();
+  }
 
   const void *fn = bwd_kernel_ptr(norm_type, in_dtype, with_add, pl.cfg);
   if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no backward kernel for this combination");

@@ -76,6 +76,11 @@ constexpr int kColThreads = 512;
 const void *fwd_row_kernel_ptr(int norm, int in_dtype, int mode, int cfg);
 const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg);
 const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor);
+// general kernels (any hidden size, element-aligned tensors)
+const void *fwd_gen_row_kernel_ptr(int norm, int in_dtype, int mode);
+const void *fwd_gen_col_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor);
+const void *bwd_gen_row_kernel_ptr(int norm, int in_dtype, bool add);
+const void *bwd_gen_wgrad_kernel_ptr(int norm, int in_dtype);
 const void *bwd_kernel_ptr(int norm, int in_dtype, bool add, int cfg);
 const void *bwd_finalize_kernel_ptr();
 const void *ws_init_kernel_ptr();

@@ -22,7 +22,9 @@ Tolerances (written here, used by every parity test):
   scale_inv       bit-exact
   bf16 / f16 dx   (|g - v| - half_ulp(v)) / max(|v|, rms_row(v)) <= 2e-3: the error beyond
                   the output's own nearest rounding (bf16 alone can be 2^-8 relative away
-                  from v just above a power of two, more than 2e-3)
+                  from v just above a power of two, more than 2e-3); for rows of fewer than
+                  8 elements, whose summands cancel, the denominator also takes the summands'
+                  magnitude rsigma * |dy * g|
   dgamma, dbeta   |g - v| / max(|v|, rms(v)) <= 1e-4
 """
 from __future__ import annotations
@@ -220,12 +222,17 @@ def half_ulp(v, dtype):
     return np.ldexp(0.5, (np.maximum(e, fmt.emin) - fmt.mant_bits).astype(np.int64))
 
 
-def check_dx(dx_g, v, dtype):
+def check_dx(dx_g, v, dtype, terms=None):
     """dx against unrounded v: the error beyond the output's own nearest rounding (half an
-    ulp of the storage format) must stay within the relative tolerance."""
+    ulp of the storage format) must stay within the relative tolerance. terms (optional,
+    laid out like v): the magnitude rsigma * |dy * g| of the summands of dx, for rows so short
+    that the summands cancel (a row of one element has dx = rsigma * w * (1 - xhat^2), a
+    difference of nearly equal binary32 values); the error is then measured against them."""
     g = np.asarray(dx_g, np.float64) if dtype == "f32" else F.decode_storage(np.asarray(dx_g), dtype)
     rms = np.sqrt(np.mean(v * v, axis=-1, keepdims=True))
     den = np.maximum(np.abs(v), rms)
+    if terms is not None:
+        den = np.maximum(den, np.asarray(terms, np.float64))
     excess = np.maximum(np.abs(g - v) - half_ulp(v, dtype), 0.0)
     err = excess / np.where(den > 0, den, 1.0)
     tol = TOL["f32"] if dtype == "f32" else TOL["dx16"]

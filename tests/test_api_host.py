@@ -94,11 +94,14 @@ def test_bwd_workspace_queries():
     assert bwd_ws(32768, 8192, norm=L.NORM_RMSNORM, add=1)[0] == L.NORM_OK
     assert bwd_ws(32768, 8192, norm=L.NORM_LAYERNORM, add=1)[0] == L.NORM_ERR_INVALID_ARG
     assert bwd_ws(10, 4096)[1] <= n                                    # monotone in rows
-    assert bwd_ws(16, 1 << 20)[0] == L.NORM_ERR_UNSUPPORTED            # beyond this build's backward
+    rc2, n2 = bwd_ws(16, 1 << 20)                                      # beyond the row layouts: general kernels
+    assert rc2 == L.NORM_OK and n2 >= L.NORM_WS_HEADER_BYTES + 256 * (1 << 20) * 4
+    assert bwd_ws(64, 100)[0] == L.NORM_OK                             # hidden not a multiple of 8
+    assert bwd_ws(16, (1 << 24) + 8)[0] == L.NORM_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(hidden=100), L.NORM_ERR_UNSUPPORTED),                        # not a multiple of 8
+    (dict(hidden=(1 << 24) + 8), L.NORM_ERR_UNSUPPORTED),              # beyond 2^24
     (dict(hidden=0), L.NORM_ERR_INVALID_ARG),
     (dict(rows=-1), L.NORM_ERR_INVALID_ARG),
     (dict(norm=7), L.NORM_ERR_INVALID_ARG),
@@ -137,9 +140,10 @@ def _fwd(**kw):
     (dict(y=None), L.NORM_ERR_INVALID_ARG),
     (dict(beta=FAKE), L.NORM_ERR_INVALID_ARG),                                 # beta with RMSNorm
     (dict(norm=L.NORM_LAYERNORM), L.NORM_ERR_INVALID_ARG),                     # LayerNorm without beta
-    (dict(x=FAKE + 4), L.NORM_ERR_MISALIGNED),
-    (dict(y=FAKE + 8), L.NORM_ERR_MISALIGNED),
-    (dict(hidden=60), L.NORM_ERR_UNSUPPORTED),
+    (dict(x=FAKE + 1), L.NORM_ERR_MISALIGNED),                                 # not element-aligned
+    (dict(y=FAKE + 1), L.NORM_ERR_MISALIGNED),
+    (dict(rs=FAKE + 2), L.NORM_ERR_MISALIGNED),
+    (dict(hidden=(1 << 24) + 8), L.NORM_ERR_UNSUPPORTED),
     (dict(eps=-1.0), L.NORM_ERR_INVALID_ARG),
     (dict(margin=-1), L.NORM_ERR_INVALID_ARG),
     (dict(y_col=FAKE), L.NORM_ERR_INVALID_ARG),                                # colwise buffer, rowwise layout
@@ -179,9 +183,10 @@ def _bwd(**kw):
     (dict(norm=L.NORM_RMSNORM), L.NORM_ERR_INVALID_ARG),          # dbeta given for RMSNorm
     (dict(ws=None), L.NORM_ERR_INVALID_ARG),
     (dict(wsb=1000), L.NORM_ERR_WORKSPACE_TOO_SMALL),
-    (dict(dx=FAKE + 2), L.NORM_ERR_MISALIGNED),
-    (dict(hidden=12), L.NORM_ERR_UNSUPPORTED),
-    (dict(hidden=1 << 20), L.NORM_ERR_UNSUPPORTED),
+    (dict(dx=FAKE + 1), L.NORM_ERR_MISALIGNED),                    # not element-aligned
+    (dict(rs=FAKE + 2), L.NORM_ERR_MISALIGNED),
+    (dict(in_dt=L.NORM_FP8_E4M3), L.NORM_ERR_UNSUPPORTED),
+    (dict(hidden=(1 << 24) + 8), L.NORM_ERR_UNSUPPORTED),
 ])
 def test_bwd_rejects_before_enqueue(kw, code):
     assert _bwd(**kw) == code
