@@ -175,7 +175,7 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   if (row_override >= 0 && row_override < ROW_NCFG && kRowShapes[row_override].cover() >= hidden) {
     row_cfg = row_override;
   } else {
-    const int pref[] = {ROW_W1_K1, ROW_W1_K2, ROW_W1_K4, ROW_W1_K8, ROW_W4_K4, ROW_W8_K4, ROW_W16_K8};
+    const int pref[] = {ROW_W1_K1, ROW_W1_K2, ROW_W1_K4, ROW_W2T2_K4, ROW_W4_K4, ROW_W8_K4, ROW_W16_K8};
     for (int c : pref)
       if (kRowShapes[c].cover() >= hidden) {
         row_cfg = c;

@@ -138,6 +138,35 @@ __device__ __forceinline__ void load_w8(float (&o)[8], const void *base, int64_t
     }
   }
 }
+// the same in two steps, so that the loads can run ahead of their use: load_w8_raw issues two
+// 16-byte loads whatever the dtype (a 16-bit weight array reads its 16 bytes twice) and keeps
+// the raw bits; w8_convert turns them into floats where they are used (converting at the load
+// would make the compiler wait there for every load in flight)
+struct W8Raw {
+  uint4 a, c;
+};
+__device__ __forceinline__ void load_w8_raw(W8Raw &w, const void *base, uint32_t elem, int dt) {
+  const bool f32 = dt == DT_F32;
+  const uint32_t off = elem * (f32 ? 4u : 2u);
+  const char *b = static_cast<const char *>(base);
+  w.a = *reinterpret_cast<const uint4 *>(b + off);
+  w.c = *reinterpret_cast<const uint4 *>(b + (off + (f32 ? 16u : 0u)));
+}
+__device__ __forceinline__ void w8_convert(float (&o)[8], const W8Raw &w, int dt) {
+  if (dt == DT_F32) {
+    const uint32_t v[8] = {w.a.x, w.a.y, w.a.z, w.a.w, w.c.x, w.c.y, w.c.z, w.c.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = __uint_as_float(v[i]);
+  } else if (dt == DT_BF16) {
+    Strip<BF16> s;
+    s.v[0] = w.a;
+    strip_to_f32<BF16>(s, o);
+  } else {
+    Strip<F16> h;
+    h.v[0] = w.a;
+    strip_to_f32<F16>(h, o);
+  }
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   __bf16 ha = (__bf16)a, hb = (__bf16)b;  // v_cvt_pk_bf16_f32: nearest-even

@@ -23,13 +23,22 @@
 
 namespace nf8 {
 
+#ifndef NF8_WLA
+#define NF8_WLA 1
+#endif
+
 // WL: where the weights live while the workgroup walks its rows. 0: each lane keeps its
 // columns' gamma / beta in registers; 1: the workgroup stages them once in LDS (as float32,
 // 1 + gamma when zero-centred), leaving the registers to the row data so that the next row
 // can be in flight while the current one is normalised; 2 (rows too long for either): each
 // strip's weights are read where they are used (they stay in the L2 across rows).
+// waves per SIMD the compiler must leave room for: the 8-wave long-row layout is meant to run two
+// workgroups per compute unit
+template <int P, int T, int KC> constexpr int row_min_waves() { return P * T == 8 && KC == 16 ? 4 : 1; }
+
 template <int NORM, class IN, int MODE, int P, int T, int KC, int WL>
-__global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
+__global__ __launch_bounds__(64 * P * T) __attribute__((amdgpu_waves_per_eu(row_min_waves<P, T, KC>())))
+void fwd_row_kernel(FwdRowParams p) {
   constexpr int TEAM = 64 * P;
   constexpr int NT = TEAM * T;
   constexpr int COVER = 8 * TEAM * KC;                      // row elements one team holds
@@ -101,20 +110,30 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
     }
   }
   // the 8 weights of strip k (from LDS or registers)
+  // WL == 2: strip k's raw weights are loaded ahead of their use and converted where used
+  auto weights_raw = [&](int k, W8Raw &rg, W8Raw &rb) {
+    uint32_t c = cv[k] ? 8u * (uint32_t)(tl + TEAM * k) : 0u;
+    // formed where it is used (a scalar base plus this 32-bit offset) rather than hoisted out
+    // of the row loop as 64-bit addresses held for every strip
+    asm volatile("" : "+v"(c));
+    load_w8_raw(rg, p.gamma, c, p.w_dtype);
+    if constexpr (NORM == NT_LAYERNORM) load_w8_raw(rb, p.beta, c, p.w_dtype);
+  };
+  auto weights_cvt = [&](int k, const W8Raw &rg, const W8Raw &rb, float (&gk)[8], float (&bk)[8]) {
+    w8_convert(gk, rg, p.w_dtype);
+    if constexpr (NORM == NT_LAYERNORM) w8_convert(bk, rb, p.w_dtype);
+    const float z = p.zero_centered ? 1.0f : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // strips past the end read column 0: zero them
+      gk[i] = cv[k] ? gk[i] + z : 0.0f;
+      if constexpr (NORM == NT_LAYERNORM) bk[i] = cv[k] ? bk[i] : 0.0f;
+    }
+  };
   auto weights = [&](int k, float (&gk)[8], float (&bk)[8]) {
     if constexpr (WL == 2) {
-      const int64_t c = 8 * (int64_t)(tl + TEAM * k);
-      if (cv[k]) {
-        load_w8(gk, p.gamma, c, p.w_dtype);
-        if (p.zero_centered) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) gk[i] += 1.0f;
-        }
-        if constexpr (NORM == NT_LAYERNORM) load_w8(bk, p.beta, c, p.w_dtype);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) gk[i] = bk[i] = 0.0f;
-      }
+      W8Raw rg, rb;
+      weights_raw(k, rg, rb);
+      weights_cvt(k, rg, rb, gk, bk);
     } else if constexpr (WL == 1) {
       const int c = 8 * (tl + TEAM * k);
       const float4 *s0 = reinterpret_cast<const float4 *>(wlds + c);
@@ -159,7 +178,8 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   };
 
   // software pipeline: the next row's loads are issued before the current row is normalised
-  // (not with WL == 2: the registers hold the weights in flight instead)
+  // (not with WL == 2: the registers hold the weights in flight instead, and two workgroups per
+  // compute unit overlap one's loads with the other's normalisation)
   constexpr bool PF = WL != 2;
   Strip<IN> cur[KC], nxt[PF ? KC : 1];
   int64_t base = (int64_t)blockIdx.x * T;
@@ -172,6 +192,16 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
     if (H != COVER) {  // strips past the end of the row read column 0: zero them
 #pragma unroll
       for (int k = 0; k < KC; ++k) mask_strip<IN>(cur[k], cv[k]);
+    }
+    // WL == 2: the weights of strip k are loaded WLA strips ahead of their use (WLA + 1
+    // buffers in turn); the first ones go out before the statistics so their latency hides
+    // behind them
+    constexpr int WLA = NF8_WLA;
+    constexpr int WQ = WL == 2 && MODE != MODE_STATS ? WLA + 1 : 1;
+    W8Raw wq_g[WQ], wq_b[WQ];
+    if constexpr (WQ > 1) {
+#pragma unroll
+      for (int k = 0; k < WLA && k < KC; ++k) weights_raw(k, wq_g[k], wq_b[k]);
     }
 
     // ---- lane-local statistics over its valid strips
@@ -280,7 +310,12 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
       const bool ok = rv && cv[k];
       const int64_t col = 8 * (int64_t)(tl + TEAM * k);
       float gk[8], bk[8], xv[8], y[8];
-      weights(k, gk, bk);
+      if constexpr (WQ > 1) {
+        if (k + WLA < KC) weights_raw(k + WLA, wq_g[(k + WLA) % WQ], wq_b[(k + WLA) % WQ]);
+        weights_cvt(k, wq_g[k % WQ], wq_b[k % WQ], gk, bk);
+      } else {
+        weights(k, gk, bk);
+      }
       strip_to_f32<IN>(cur[k], xv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -321,6 +356,8 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
 #pragma unroll
       for (int k = 0; k < KC; ++k) cur[k] = nxt[k];
     } else {
+      // (loads return in issue order: the next row's loads go out after the last weight load
+      // this row needs, or every weight load behind them would wait for HBM)
       load_row(cur, base + stride + team);
     }
   }
@@ -374,6 +411,7 @@ static const void *pick_cfg(int cfg) {
     case ROW_W8_K1: return NF8_ROW(8, 1, 1);
     case ROW_W4T2_K2: return NF8_ROW(4, 2, 2);
     case ROW_W16_K8: return NF8_ROW(16, 1, 8);
+    case ROW_W8_K16: return NF8_ROW(8, 1, 16);
     default: return nullptr;
   }
 #undef NF8_ROW

@@ -111,7 +111,7 @@ def test_fwd_plain_other_out_dtype_and_bf16_weights(out_dt):
     checks.check_hp(bits(out["y"]), ref["v"], out_dt, terms=ln_terms(case, ref, "layernorm", "bf16"))
 
 
-ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096, 65536]   # per row layout
+ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096, 65536, 65536]   # per row layout
 BWD_COVER = [1024, 2048, 4096, 8192, 16384, 4096, 8192, 8192, 1024, 2048, 4096]
 
 
@@ -128,6 +128,39 @@ def test_fwd_every_row_layout(cfg, norm):
     checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
                        out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
     checks.check_hp(bits(out["y"]), ref["v"], "bf16", terms=ln_terms(case, ref, norm))
+
+
+# rows longer than 16384 elements: the 16-wave layout whose weights are read from the caches a
+# strip ahead of their use (any weight dtype, zero-centred gamma, every rowwise epilogue)
+@pytest.mark.parametrize("w_dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("mode", ["none", "delayed", "mxfp8"])
+@pytest.mark.parametrize("norm,hidden,zc", [("layernorm", 65536, False), ("rmsnorm", 65536, True),
+                                            ("layernorm", 40000, True), ("rmsnorm", 20488, False)])
+def test_fwd_long_rows(w_dt, mode, norm, hidden, zc):
+    rows = 5
+    case = workloads.small_case(norm, rows, hidden, "bf16", w_dt, seed=hidden % 97 + rows, zero_centered_gamma=zc)
+    ref = oracle_fwd(case, norm, "bf16", w_dt, zc)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    t = ln_terms(case, ref, norm, w_dt, zc)
+    if mode == "none":
+        out = nf.fwd(x, g, b, norm=norm, eps=EPS, zero_centered_gamma=zc)
+        checks.check_hp(bits(out["y"]), ref["v"], "bf16", terms=t)
+    elif mode == "delayed":
+        scale = float(np.float32(F.E4M3.max_finite) / np.float32(np.max(np.abs(ref["v"]))))
+        st = torch.tensor([scale], dtype=torch.float32, device="cuda")
+        am = torch.zeros(1, dtype=torch.float32, device="cuda")
+        out = nf.fwd(x, g, b, norm=norm, eps=EPS, zero_centered_gamma=zc, scaling="delayed", fp8="e4m3",
+                     scale=st, amax=am, layout="rowwise")
+        got = {"y": bits(out["y"]), "y_colwise": None, "scale_inv": out["scale_inv"].item(),
+               "colwise_scale_inv": None, "amax": out["amax"].item()}
+        checks.check_delayed(got, ref["v"], scale, 0.0, "e4m3", rowwise=True, colwise=False, terms=t)
+    else:
+        out = nf.fwd(x, g, b, norm=norm, eps=EPS, zero_centered_gamma=zc, scaling="mxfp8", fp8="e4m3",
+                     layout="rowwise")
+        checks.check_mx_rows(bits(out["y"]), bits(out["scale_inv"]), ref["v"], "e4m3", "mx rowwise", terms=t)
+    checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
+                       out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+    assert_ws_clean()
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
