@@ -32,13 +32,8 @@ namespace nf8 {
 // 1 + gamma when zero-centred), leaving the registers to the row data so that the next row
 // can be in flight while the current one is normalised; 2 (rows too long for either): each
 // strip's weights are read where they are used (they stay in the L2 across rows).
-// waves per SIMD the compiler must leave room for: the 8-wave long-row layout is meant to run two
-// workgroups per compute unit
-template <int P, int T, int KC> constexpr int row_min_waves() { return P * T == 8 && KC == 16 ? 4 : 1; }
-
 template <int NORM, class IN, int MODE, int P, int T, int KC, int WL>
-__global__ __launch_bounds__(64 * P * T) __attribute__((amdgpu_waves_per_eu(row_min_waves<P, T, KC>())))
-void fwd_row_kernel(FwdRowParams p) {
+__global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   constexpr int TEAM = 64 * P;
   constexpr int NT = TEAM * T;
   constexpr int COVER = 8 * TEAM * KC;                      // row elements one team holds
@@ -411,7 +406,6 @@ static const void *pick_cfg(int cfg) {
     case ROW_W8_K1: return NF8_ROW(8, 1, 1);
     case ROW_W4T2_K2: return NF8_ROW(4, 2, 2);
     case ROW_W16_K8: return NF8_ROW(16, 1, 8);
-    case ROW_W8_K16: return NF8_ROW(8, 1, 16);
     default: return nullptr;
   }
 #undef NF8_ROW

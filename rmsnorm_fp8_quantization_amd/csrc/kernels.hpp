@@ -19,7 +19,6 @@ enum RowCfg : int {
   ROW_W8_K1,
   ROW_W4T2_K2,  // 4 waves per row, 2 rows per workgroup
   ROW_W16_K8,   // 16 waves per row (long rows, weights read from the caches per strip)
-  ROW_W8_K16,   // 8 waves per row, two workgroups per compute unit (long rows of 16-bit input)
   ROW_NCFG
 };
 struct RowShape {
@@ -28,8 +27,7 @@ struct RowShape {
   int64_t cover() const { return 512LL * P * KC; }  // row elements one team holds
 };
 constexpr RowShape kRowShapes[ROW_NCFG] = {{1, 4, 1}, {1, 4, 2}, {1, 4, 4}, {1, 4, 8}, {4, 1, 2}, {4, 1, 4},
-                                           {8, 1, 4}, {2, 2, 4}, {8, 1, 1}, {4, 2, 2}, {16, 1, 8},
-                                           {8, 1, 16}};
+                                           {8, 1, 4}, {2, 2, 4}, {8, 1, 1}, {4, 2, 2}, {16, 1, 8}};
 
 // ---- forward band kernel: 4 waves, RW rows per wave, KC strips per lane
 enum BandCfg : int { BAND_R8_K1 = 0, BAND_R8_K2, BAND_R4_K2, BAND_R1_K4, BAND_R2_K8, BAND_NCFG };
