@@ -438,10 +438,16 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     int occ = 1;
     int r = occupancy(fn, sh.threads(), &occ);
     if (r) return r;
-    int64_t grid = cdiv(rows, sh.T);
+    const int occ_cap = env_int("NORMFP8_ROW_OCC", 0);  // tuning: fewer workgroups per CU
+    if (occ_cap > 0 && occ_cap < occ) occ = occ_cap;
+    const int64_t slots = cdiv(rows, sh.T);
     int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
     if (cap > kMaxGrid) cap = kMaxGrid;
-    if (grid > cap) grid = cap;
+    // persistent grid: as many workgroups as give every one the same number of rows, so that
+    // the last round does not run on a fraction of the grid
+    const int64_t rounds = cdiv(slots, cap < 1 ? 1 : cap);
+    int64_t grid = cdiv(slots, rounds < 1 ? 1 : rounds);
+    if (env_int("NORMFP8_ROW_BALANCE", 1) == 0) grid = slots < cap ? slots : cap;
     if (grid < 1) grid = 1;
     FwdRowParams copy = rp;
     return launch(fn, dim3((unsigned)grid), dim3(sh.threads()), &copy, st);

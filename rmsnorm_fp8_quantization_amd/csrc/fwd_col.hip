@@ -316,7 +316,12 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
         } else {
           uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + T.c0 * tp.mx_rows + 4 * (int64_t)T.rt +
                          (size_t)((uint32_t)tid * (uint32_t)tp.mx_rows);
-          for (int q = 0; q < nb; ++q) dst[q] = colx[q][tid];
+          if (nb == 4 && ((uintptr_t)dst & 3) == 0) {  // one 4-byte store rather than four byte stores
+            *reinterpret_cast<uint32_t *>(dst) = (uint32_t)colx[0][tid] | ((uint32_t)colx[1][tid] << 8) |
+                                                 ((uint32_t)colx[2][tid] << 16) | ((uint32_t)colx[3][tid] << 24);
+          } else {
+            for (int q = 0; q < nb; ++q) dst[q] = colx[q][tid];
+          }
         }
       }
     }
