@@ -27,7 +27,9 @@
 // (two buffers, used in turn) as [column][128 rows] with 16-byte groups XOR-swizzled across
 // banks, and stored so that 8 consecutive lanes write a column's 128-byte line. An MXFP8
 // columnwise block (32 rows) is two waves: each wave reduces its 16 rows per column and the
-// pair combine through LDS.
+// pair combine through LDS. (The tile height is NF8_COL_TILE_ROWS, 128 by default; 256 builds a
+// 16-wave variant whose columns are 256-byte pieces, which measured slower: one workgroup per
+// CU instead of two.)
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -35,9 +37,12 @@ namespace nf8 {
 
 namespace {
 
-constexpr int kTR = kColTileRows;  // 128 rows per tile (one 128-byte line per column)
+constexpr int kTR = kColTileRows;  // rows per tile (kTR bytes of each column's codes)
 constexpr int kTC = kColTileCols;  // 128 columns per tile (one 128-byte line per row)
-static_assert(kTR == 128 && kTC == 128, "tile shape");
+constexpr int kWaves = kColThreads / 64;  // 16 rows per wave
+constexpr int kBlk = kTR / 32;            // MXFP8 columnwise blocks per tile column
+constexpr int kLanesPerCol = kTR / 16;    // lanes that store one column's kTR bytes
+static_assert((kTR == 128 || kTR == 256) && kTC == 128 && kWaves * 16 == kTR, "tile shape");
 
 // 4 x 4 byte transpose: byte r of word c of the result is byte c of input word r
 __device__ __forceinline__ void transpose4x4b(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
@@ -69,7 +74,7 @@ __device__ __forceinline__ float rowgroup_max(float v) {
 template <int NORM, class IN, int MODE, bool CRM>
 __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp) {
   static_assert(MODE == MODE_DELAYED || MODE == MODE_MX, "columnwise output is FP8");
-  static_assert(kColThreads == 512, "8 waves of 16 rows");
+
   const FwdRowParams &p = tp.f;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -89,8 +94,8 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
   const int cloc = 8 * cl;              // this lane's first column within a tile
 
   __shared__ __align__(16) uint8_t stage[2][kTC * kTR];
-  __shared__ __align__(16) float cmax[MODE == MODE_MX ? 8 : 1][MODE == MODE_MX ? kTC : 4];
-  __shared__ uint8_t colx[MODE == MODE_MX ? 4 : 1][MODE == MODE_MX ? kTC : 1];
+  __shared__ __align__(16) float cmax[MODE == MODE_MX ? kWaves : 1][MODE == MODE_MX ? kTC : 4];
+  __shared__ uint8_t colx[MODE == MODE_MX ? kBlk : 1][MODE == MODE_MX ? kTC : 1];
   __shared__ uint32_t s_last, s_epoch;
   __shared__ float wred[kColThreads / 64];
 
@@ -289,10 +294,10 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
     // ---- columnwise stores: thread (c, m) writes rows [16m, 16m + 16) of tile column c
     const bool full = T.rows_here == kTR && (N % 16) == 0;
     uint8_t *const yct = static_cast<uint8_t *>(tp.y_col) + T.c0 * N + T.r0;
-    const int m = tid & 7;
+    const int m = tid % kLanesPerCol;
 #pragma unroll
     for (int pass = 0; pass < (CRM ? 0 : kTC / 64); ++pass) {
-      const int c = pass * 64 + (tid >> 3);
+      const int c = pass * 64 + tid / kLanesPerCol;
       if (c < T.cols_here) {
         const uint4 v = *reinterpret_cast<const uint4 *>(stg + stage_off(c, 4 * m));
         uint8_t *dst = yct + (size_t)((uint32_t)c * Nu + (uint32_t)(16 * m));
@@ -311,14 +316,17 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
       if (tid < T.cols_here) {
         const int nb = (T.rows_here + 31) / 32;
         if constexpr (CRM) {  // [ceil(rows/32), hidden]: one 128-byte run per block row
-          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + 4 * (int64_t)T.rt * H + T.c0 + tid;
+          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + kBlk * (int64_t)T.rt * H + T.c0 + tid;
           for (int q = 0; q < nb; ++q) dst[(size_t)q * Hu] = colx[q][tid];
         } else {
-          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + T.c0 * tp.mx_rows + 4 * (int64_t)T.rt +
+          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + T.c0 * tp.mx_rows + kBlk * (int64_t)T.rt +
                          (size_t)((uint32_t)tid * (uint32_t)tp.mx_rows);
-          if (nb == 4 && ((uintptr_t)dst & 3) == 0) {  // one 4-byte store rather than four byte stores
-            *reinterpret_cast<uint32_t *>(dst) = (uint32_t)colx[0][tid] | ((uint32_t)colx[1][tid] << 8) |
-                                                 ((uint32_t)colx[2][tid] << 16) | ((uint32_t)colx[3][tid] << 24);
+          if (nb == kBlk && ((uintptr_t)dst & (kBlk - 1)) == 0) {  // one store rather than kBlk byte stores
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int q = 0; q < kBlk; ++q) w[q >> 2] |= (uint32_t)colx[q][tid] << (8 * (q & 3));
+            if constexpr (kBlk == 8) *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+            else *reinterpret_cast<uint32_t *>(dst) = w[0];
           } else {
             for (int q = 0; q < nb; ++q) dst[q] = colx[q][tid];
           }

@@ -69,9 +69,12 @@ constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1, 4}, {4, 1, 2}, {4, 2, NF8_BWD_
                                            {2, 1, 1}, {4, 1, 1}, {4, 2, 1}};
 
 // ---- forward tile kernel (second pass of a columnwise output): 8 waves, 128 x 128 tiles
-constexpr int kColTileRows = 128;
+#ifndef NF8_COL_TILE_ROWS
+#define NF8_COL_TILE_ROWS 128
+#endif
+constexpr int kColTileRows = NF8_COL_TILE_ROWS;
 constexpr int kColTileCols = 128;
-constexpr int kColThreads = 512;
+constexpr int kColThreads = 4 * kColTileRows;  // 16 rows per wave
 
 const void *fwd_row_kernel_ptr(int norm, int in_dtype, int mode, int cfg);
 const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg);
