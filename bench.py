@@ -9,8 +9,10 @@ of consecutive steps exceeds the 256 MB Infinity Cache. Inputs are resident in H
 the timed region starts.
 
 Printed: one JSON line. `value` is achieved GB/s = minimal algorithmic bytes of the step
-(each input read once, each output written once) / step time; `roofline` gives the dominant
-call (the backward) against the 8 TB/s HBM peak, timed with HIP events on the launch stream;
+(each input read once, each output written once) / step time, the steps timed back to back
+with nothing between the launches; `roofline` gives the dominant call (the backward) against
+the 8 TB/s HBM peak, its average launch duration taken over back-to-back launches of that
+call bracketed by HIP events on the launch stream;
 `cpu_baseline` times the float64 CPU oracle on a bounded row sample of the same workload;
 `workloads` reports every other workload of the benchmark's list the same way.
 """
@@ -126,38 +128,47 @@ def run_workload(w: W.Workload, nf, steps: int, warmup: int, headline: bool):
             bcalls.append(bc)
     torch.cuda.synchronize()
 
-    def step(k, ev=None):
+    def step(k):
         i = k % sets
         j = (k - 1) % sets
         if has_fwd:
-            if ev is not None:
-                ev[0].record(st)
             fcalls[i]()
-            if ev is not None:
-                ev[1].record(st)
         if has_bwd:
-            if ev is not None:
-                ev[2].record(st)
             bcalls[j]()
-            if ev is not None:
-                ev[3].record(st)
 
     for k in range(max(warmup, sets)):
         step(k)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    # the timed region: exactly `steps` steps with nothing between the launches (an event
+    # recorded between two kernels adds a gap to the stream)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(st)
     for k in range(steps):
-        step(warmup + k, evs[k])
+        step(warmup + k)
     t1.record(st)
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
-    fwd_us = [ev[0].elapsed_time(ev[1]) * 1e3 for ev in evs] if has_fwd else []
-    bwd_us = [ev[2].elapsed_time(ev[3]) * 1e3 for ev in evs] if has_bwd else []
+    # the per-call breakdown: each call's average launch duration over `steps` back-to-back
+    # launches on rotating buffer sets, bracketed by two HIP events on the launch stream (three
+    # such runs; an event recorded between every two launches would add its own gap to each)
+    def per_call(calls):
+        out = []
+        for _ in range(3):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(st)
+            for k in range(steps):
+                calls[k % len(calls)]()
+            b.record(st)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) * 1e3 / steps)
+        return out
+    fwd_us = per_call(fcalls) if has_fwd else []
+    bwd_us = per_call(bcalls) if has_bwd else []
 
     res = {"rows": w.rows, "hidden": w.hidden, "norm": w.norm, "in_dtype": w.in_dtype,
            "scaling": w.scaling, "colwise": w.colwise, "step_ms": step_ms}
