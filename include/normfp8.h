@@ -83,7 +83,10 @@ typedef enum {
   NORM_Q_ROWWISE_COLWISE = 3,
   /* modifier, with NORM_Q_COLWISE: the columnwise output keeps the rowwise [rows, hidden] layout
      (codes of the columnwise quantisation in place, MXFP8 scales [ceil(rows/32), hidden]) */
-  NORM_Q_COLWISE_ROWMAJOR = 4
+  NORM_Q_COLWISE_ROWMAJOR = 4,
+  /* modifier, MXFP8 only: E8M0 grids padded for consumers that read scales in whole tiles
+     (see norm_fwd) */
+  NORM_Q_SCALES_PADDED = 8
 } norm_qlayout_t;
 
 /*
@@ -144,6 +147,14 @@ int norm_bwd_workspace_size(int64_t rows, int64_t hidden, int in_dtype, int w_dt
  *     (element (r, c) holds the code the transposed layout keeps at (c, r)) and the MXFP8
  *     colwise_scale_inv is uint8 [ceil(rows/32), hidden]; this build serves it for rows that a
  *     row layout covers (hidden <= 65536) and returns NORM_ERR_UNSUPPORTED otherwise.
+ *   With NORM_Q_SCALES_PADDED added (MXFP8 only; for callers that hand the E8M0 grids to
+ *     matrix-multiply kernels reading scales in whole tiles): in each grid the dimension that
+ *     counts 32-element blocks is rounded up to a multiple of 4 and the other dimension to a
+ *     multiple of 128, so scale_inv is [round_up(rows, 128), round_up(ceil(hidden/32), 4)],
+ *     colwise_scale_inv [round_up(hidden, 128), round_up(ceil(rows/32), 4)], or with
+ *     NORM_Q_COLWISE_ROWMAJOR [round_up(ceil(rows/32), 4), round_up(hidden, 128)]. The kernels
+ *     write the logical region only; the padding keeps whatever the caller put there. The
+ *     pages name no padded layout: this is a reading, its parity with the pages' system unpinned.
  *   The layout pointers not requested by qlayout must be NULL.
  *
  *   Errors: NORM_ERR_INVALID_ARG for NULL required pointers or bad codes; NORM_ERR_UNSUPPORTED

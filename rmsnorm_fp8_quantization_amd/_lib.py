@@ -20,6 +20,7 @@ NORM_LAYERNORM, NORM_RMSNORM = 0, 1
 NORM_F32, NORM_F16, NORM_BF16, NORM_FP8_E4M3, NORM_FP8_E5M2 = range(5)
 NORM_SCALING_NONE, NORM_SCALING_DELAYED_TENSOR, NORM_SCALING_MXFP8_1D32, NORM_SCALING_MXFP8_1D32_CEIL = range(4)
 NORM_Q_ROWWISE, NORM_Q_COLWISE, NORM_Q_ROWWISE_COLWISE, NORM_Q_COLWISE_ROWMAJOR = 1, 2, 3, 4
+NORM_Q_SCALES_PADDED = 8
 NORM_WS_HEADER_BYTES = 16384
 
 EXPORTS = ("norm_fwd_workspace_size", "norm_bwd_workspace_size", "norm_fwd", "norm_bwd",

@@ -129,6 +129,7 @@ struct FwdPlan {
   size_t partial_off = 0;
   size_t stats_off = 0;  // two-pass path: mu / rsigma when the caller passes none
   bool col_rowmajor = false;
+  bool scales_padded = false;  // MXFP8 E8M0 grids padded (block dimension to 4, the other to 128)
   bool gen = false;   // general kernels: hidden not a multiple of 8 (or, at launch, unaligned tensors)
 };
 
@@ -140,6 +141,8 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   if (!is_hp(in_dtype)) return fail(NORM_ERR_UNSUPPORTED, "input dtype %d not supported", in_dtype);
   if (!is_hp(w_dtype)) return fail(NORM_ERR_UNSUPPORTED, "weight dtype %d not supported", w_dtype);
   if (cu_margin < 0) return fail(NORM_ERR_INVALID_ARG, "cu_margin must be >= 0");
+  const bool scales_padded = (qlayout & NORM_Q_SCALES_PADDED) != 0;
+  qlayout &= ~NORM_Q_SCALES_PADDED;
   const bool col_rowmajor = (qlayout & NORM_Q_COLWISE_ROWMAJOR) != 0;
   if (col_rowmajor) {
     if (!(qlayout & NORM_Q_COLWISE))
@@ -165,6 +168,9 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     default:
       return fail(NORM_ERR_INVALID_ARG, "unknown scaling mode %d", scaling);
   }
+  if (scales_padded && pl->mode != MODE_MX)
+    return fail(NORM_ERR_INVALID_ARG, "NORM_Q_SCALES_PADDED applies to MXFP8 scaling only");
+  pl->scales_padded = scales_padded;
   pl->rowwise = (qlayout & NORM_Q_ROWWISE) != 0;
   pl->colwise = (qlayout & NORM_Q_COLWISE) != 0;
 
@@ -424,7 +430,12 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   f.ws = static_cast<uint32_t *>(workspace);
   f.rows = rows;
   f.hidden = hidden;
-  f.mx_cols = cdiv(hidden, 32);
+  // E8M0 grid row strides (padded: the block-count dimension to a multiple of 4, the other
+  // dimension, which only the allocation sees, to a multiple of 128)
+  f.mx_cols = pl.scales_padded ? (int64_t)round_up((size_t)cdiv(hidden, 32), 4) : cdiv(hidden, 32);
+  const int64_t col_ld = pl.col_rowmajor ? (pl.scales_padded ? (int64_t)round_up((size_t)hidden, 128) : hidden)
+                                         : (pl.scales_padded ? (int64_t)round_up((size_t)cdiv(rows, 32), 4)
+                                                             : cdiv(rows, 32));
   f.w_dtype = w_dtype;
   f.out_dtype = out_dtype;
   f.mx_ceil = scaling == NORM_SCALING_MXFP8_1D32_CEIL ? 1 : 0;
@@ -488,6 +499,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
       tp.st_mu = st_mu;
       tp.st_rs = st_rs;
       tp.mx_rows = cdiv(rows, 32);
+      tp.mx_col_ld = col_ld;
       tp.col_rowmajor = pl.col_rowmajor ? 1 : 0;
       const void *fc = fwd_gen_col_kernel_ptr(norm_type, in_dtype, pl.mode, pl.col_rowmajor);
       if (!fc) return fail(NORM_ERR_UNSUPPORTED, "no general columnwise kernel for this combination");
@@ -522,6 +534,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     tp.st_mu = st_mu;
     tp.st_rs = st_rs;
     tp.mx_rows = cdiv(rows, 32);
+      tp.mx_col_ld = col_ld;
     tp.tiles_r = cdiv(rows, kColTileRows);
     tp.tiles_c = cdiv(hidden, kColTileCols);
     tp.write_row = pl.rowwise ? 1 : 0;
@@ -547,6 +560,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   b.partials = pl.S > 1 ? reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + pl.partial_off) : nullptr;
   b.bands = pl.bands;
   b.mx_rows = cdiv(rows, 32);
+  b.mx_col_ld = col_ld;
   b.S = pl.S;
   b.write_row = pl.rowwise ? 1 : 0;
   const void *fn = fwd_band_kernel_ptr(norm_type, in_dtype, pl.mode, pl.colwise, pl.cfg);

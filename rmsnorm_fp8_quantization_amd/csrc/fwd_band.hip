@@ -391,7 +391,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
             if (wave == 0) {
 #pragma unroll
               for (int i = 0; i < 8; ++i)
-                static_cast<uint8_t *>(bp.col_scale_inv)[(col + i) * bp.mx_rows + band] = (uint8_t)(colx[i] + 127);
+                static_cast<uint8_t *>(bp.col_scale_inv)[(col + i) * bp.mx_col_ld + band] = (uint8_t)(colx[i] + 127);
             }
           }
         }

@@ -315,12 +315,12 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
       // the tile's (up to) four 32-row block exponents of each column, consecutive bytes
       if (tid < T.cols_here) {
         const int nb = (T.rows_here + 31) / 32;
-        if constexpr (CRM) {  // [ceil(rows/32), hidden]: one 128-byte run per block row
-          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + kBlk * (int64_t)T.rt * H + T.c0 + tid;
-          for (int q = 0; q < nb; ++q) dst[(size_t)q * Hu] = colx[q][tid];
+        if constexpr (CRM) {  // [ceil(rows/32), hidden] (row stride mx_col_ld): one 128-byte run per block row
+          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + kBlk * (int64_t)T.rt * tp.mx_col_ld + T.c0 + tid;
+          for (int q = 0; q < nb; ++q) dst[(size_t)q * (size_t)tp.mx_col_ld] = colx[q][tid];
         } else {
-          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + T.c0 * tp.mx_rows + kBlk * (int64_t)T.rt +
-                         (size_t)((uint32_t)tid * (uint32_t)tp.mx_rows);
+          uint8_t *dst = static_cast<uint8_t *>(tp.col_scale_inv) + T.c0 * tp.mx_col_ld + kBlk * (int64_t)T.rt +
+                         (size_t)((uint32_t)tid * (uint32_t)tp.mx_col_ld);
           if (nb == kBlk && ((uintptr_t)dst & (kBlk - 1)) == 0) {  // one store rather than kBlk byte stores
             uint32_t w[2] = {0u, 0u};
 #pragma unroll

@@ -228,8 +228,8 @@ __global__ __launch_bounds__(64) void fwd_gen_col_kernel(FwdTileParams tp) {
       f = exp2_neg(X);
       if (cv) {
         uint8_t *sc = static_cast<uint8_t *>(tp.col_scale_inv);
-        if constexpr (CRM) sc[rb * H + c] = (uint8_t)(X + 127);
-        else sc[c * tp.mx_rows + rb] = (uint8_t)(X + 127);
+        if constexpr (CRM) sc[rb * tp.mx_col_ld + c] = (uint8_t)(X + 127);
+        else sc[c * tp.mx_col_ld + rb] = (uint8_t)(X + 127);
       }
     }
     if (cv) {

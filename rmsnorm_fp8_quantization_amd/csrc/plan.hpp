@@ -64,7 +64,7 @@ struct FwdRowParams {
   uint32_t *ws;     // workspace header (delayed scaling) or nullptr
   int64_t rows;
   int64_t hidden;
-  int64_t mx_cols;  // ceil(hidden / 32)
+  int64_t mx_cols;  // row stride of the rowwise E8M0 grid: ceil(hidden / 32), or padded to a multiple of 4
   int w_dtype;
   int out_dtype;    // plain: F32/F16/BF16; delayed / MX: E4M3/E5M2
   int zero_centered;
@@ -85,6 +85,7 @@ struct FwdBandParams {
                          // NV = 2 (mean, M2) for LayerNorm, 1 (sum of squares) for RMSNorm
   int64_t bands;         // ceil(rows / R)
   int64_t mx_rows;       // ceil(rows / 32)
+  int64_t mx_col_ld;     // row stride of the columnwise E8M0 grid (mx_rows, or padded)
   int S;                 // workgroups per band
   int classes;           // ticket classes (1 or kClasses); gridDim.x is a multiple of it
   int write_row;         // rowwise output requested
@@ -100,6 +101,8 @@ struct FwdTileParams {
   const float *st_mu;    // [rows] (LayerNorm)
   const float *st_rs;    // [rows]
   int64_t mx_rows;       // ceil(rows / 32)
+  int64_t mx_col_ld;     // row stride of the columnwise E8M0 grid: mx_rows ([hidden, mx_rows]) or
+                         // hidden ([mx_rows, hidden], col_rowmajor), or either padded
   int64_t tiles_r;       // ceil(rows / 128)
   int64_t tiles_c;       // ceil(hidden / 128)
   int write_row;         // rowwise output requested

@@ -79,11 +79,17 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return ws
 
 
+def _round_up(a: int, b: int) -> int:
+    return (a + b - 1) // b * b
+
+
 def fwd_workspace_size(rows, hidden, in_dtype, w_dtype, out_code, norm, scaling, layout,
                        zero_centered_gamma=False, eps=1e-5, cu_margin=0, training=True) -> int:
+    """layout: a layout name, or the ABI's qlayout code (modifiers included)."""
     n = ctypes.c_size_t(0)
+    code = _LAYOUT[layout] if isinstance(layout, str) else int(layout)
     L.call("norm_fwd_workspace_size", rows, hidden, _DT[in_dtype], _DT[w_dtype], out_code,
-           _NORM[norm], _SCALING[scaling], _LAYOUT[layout], int(zero_centered_gamma), eps,
+           _NORM[norm], _SCALING[scaling], code, int(zero_centered_gamma), eps,
            cu_margin, int(training), ctypes.byref(n))
     return n.value
 
@@ -101,7 +107,7 @@ def prepare_fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tenso
                 scaling: str = "none", out_dtype: Optional[torch.dtype] = None, fp8: str = "e4m3",
                 scale: Optional[torch.Tensor] = None, amax: Optional[torch.Tensor] = None,
                 layout: str = "rowwise", cu_margin: int = 0, training: bool = True,
-                amax_inplace: bool = False) -> Tuple[Dict[str, torch.Tensor], Prepared]:
+                amax_inplace: bool = False, scales_padded: bool = False) -> Tuple[Dict[str, torch.Tensor], Prepared]:
     """Allocate the forward's outputs and pack a ``norm_fwd`` call (see ``fwd``)."""
     _check(x, "x")
     _check(gamma, "gamma")
@@ -133,16 +139,25 @@ def prepare_fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tenso
         csi = torch.empty(1, dtype=torch.float32, device=dev) if colwise else None
         upd = amax if amax_inplace else torch.empty(1, dtype=torch.float32, device=dev)
     elif scaling in ("mxfp8", "mxfp8_ceil"):
-        si = torch.empty(rows, (hidden + 31) // 32, dtype=torch.uint8, device=dev) if rowwise else None
-        csi_shape = ((rows + 31) // 32, hidden) if col_rowmajor else (hidden, (rows + 31) // 32)
+        # E8M0 grids; padded: the block-count dimension to a multiple of 4, the other to 128
+        def grid(a, blocks):
+            return (_round_up(a, 128), _round_up(blocks, 4)) if scales_padded else (a, blocks)
+        si = torch.empty(*grid(rows, (hidden + 31) // 32), dtype=torch.uint8, device=dev) if rowwise else None
+        if col_rowmajor:
+            csi_shape = grid(hidden, (rows + 31) // 32)[::-1]
+        else:
+            csi_shape = grid(hidden, (rows + 31) // 32)
         csi = torch.empty(*csi_shape, dtype=torch.uint8, device=dev) if colwise else None
-    nbytes = fwd_workspace_size(rows, hidden, x.dtype, gamma.dtype, out_code, norm, scaling, layout,
+    if scales_padded and scaling not in ("mxfp8", "mxfp8_ceil"):
+        raise ValueError("scales_padded applies to MXFP8 scaling only")
+    lcode = _LAYOUT[layout] | (L.NORM_Q_SCALES_PADDED if scales_padded else 0)
+    nbytes = fwd_workspace_size(rows, hidden, x.dtype, gamma.dtype, out_code, norm, scaling, lcode,
                                 zero_centered_gamma, eps, cu_margin, training)
     ws = workspace(nbytes, dev) if nbytes else None
     args = (_stream(dev), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(scale), _ptr(amax), _ptr(y), _ptr(y_col),
             _ptr(mu), _ptr(rs), _ptr(si), _ptr(csi), _ptr(upd), _ptr(ws), ws.numel() if ws is not None else 0,
             rows, hidden, _DT[x.dtype], _DT[gamma.dtype], out_code, _NORM[norm], _SCALING[scaling],
-            _LAYOUT[layout], int(zero_centered_gamma), eps, cu_margin)
+            lcode, int(zero_centered_gamma), eps, cu_margin)
     out = {"y": y, "y_colwise": y_col, "mu": mu, "rsigma": rs, "scale_inv": si, "colwise_scale_inv": csi,
            "amax": upd}
     keep = (x, gamma, beta, scale, amax, y, y_col, mu, rs, si, csi, upd, ws)
@@ -160,7 +175,9 @@ def fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor] = Non
     (scaling "none"), fp8 ("e4m3" | "e5m2"), scale / amax (float32[1] GPU tensors, delayed
     scaling), layout ("rowwise" | "colwise" | "rowwise_colwise", or "colwise_rowmajor" /
     "rowwise_colwise_rowmajor" for a columnwise output kept in the [rows, hidden] layout, with MXFP8
-    columnwise scales [ceil(rows/32), hidden]), cu_margin, amax_inplace.
+    columnwise scales [ceil(rows/32), hidden]), cu_margin, amax_inplace, scales_padded (MXFP8:
+    E8M0 grids with the block-count dimension rounded up to a multiple of 4 and the other to a
+    multiple of 128; only the logical region is written).
     Returns ``y`` (rowwise output: out_dtype, or uint8 FP8 codes), ``y_colwise`` ([hidden, rows]
     uint8 codes), ``mu`` (LayerNorm), ``rsigma``, ``scale_inv`` / ``colwise_scale_inv``
     (float32[1] for delayed scaling, uint8 E8M0 grids for MXFP8) and ``amax`` (updated amax)."""

@@ -46,7 +46,8 @@ def test_enum_values_match_header():
                  "NORM_F32", "NORM_F16", "NORM_BF16", "NORM_FP8_E4M3", "NORM_FP8_E5M2",
                  "NORM_SCALING_NONE", "NORM_SCALING_DELAYED_TENSOR", "NORM_SCALING_MXFP8_1D32",
                  "NORM_SCALING_MXFP8_1D32_CEIL",
-                 "NORM_Q_ROWWISE", "NORM_Q_COLWISE", "NORM_Q_ROWWISE_COLWISE", "NORM_Q_COLWISE_ROWMAJOR"):
+                 "NORM_Q_ROWWISE", "NORM_Q_COLWISE", "NORM_Q_ROWWISE_COLWISE", "NORM_Q_COLWISE_ROWMAJOR",
+                 "NORM_Q_SCALES_PADDED"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == getattr(L, name), name
     m = re.search(r"#define NORM_WS_HEADER_BYTES (\d+)", src)
@@ -226,3 +227,19 @@ def test_colwise_rowmajor_layout_validation(monkeypatch):
     assert fwd_ws(16, 131072, layout=rm, **mx)[0] == L.NORM_ERR_UNSUPPORTED
     monkeypatch.setenv("NORMFP8_COL_KERNEL", "0")
     assert fwd_ws(64, 1024, layout=rm, **mx)[0] == L.NORM_ERR_UNSUPPORTED
+
+
+def test_scales_padded_layout_validation():
+    mx = dict(out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_MXFP8_1D32)
+    pad = L.NORM_Q_SCALES_PADDED
+    for lay in (L.NORM_Q_ROWWISE, L.NORM_Q_COLWISE, L.NORM_Q_ROWWISE_COLWISE,
+                L.NORM_Q_COLWISE | L.NORM_Q_COLWISE_ROWMAJOR):
+        assert fwd_ws(100, 1000, layout=lay | pad, **mx)[0] == L.NORM_OK
+    assert fwd_ws(100, 1000, layout=L.NORM_Q_ROWWISE | pad, out=L.NORM_FP8_E4M3,
+                  scaling=L.NORM_SCALING_MXFP8_1D32_CEIL)[0] == L.NORM_OK
+    # padded grids exist for MXFP8 only
+    assert fwd_ws(100, 1000, layout=L.NORM_Q_ROWWISE | pad, out=L.NORM_FP8_E4M3,
+                  scaling=L.NORM_SCALING_DELAYED_TENSOR)[0] == L.NORM_ERR_INVALID_ARG
+    assert fwd_ws(100, 1000, layout=L.NORM_Q_ROWWISE | pad)[0] == L.NORM_ERR_INVALID_ARG
+    # the modifier alone is not a layout
+    assert fwd_ws(100, 1000, layout=pad, **mx)[0] == L.NORM_ERR_INVALID_ARG

@@ -256,6 +256,70 @@ def test_fwd_mxfp8(fp8, layout, norm, rows, hidden, zc):
     assert_ws_clean()
 
 
+# padded E8M0 grids (block-count dimension to a multiple of 4, the other to 128): the same codes
+# and logical scales as the unpadded layout, the padding left as the caller filled it
+SENTINEL = 0xA5
+
+
+def _padded_case(path, layout, norm, rows, hidden):
+    case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=rows + hidden + 3)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    knobs = {"band": dict(NORMFP8_FORCE_BAND=1, NORMFP8_COL_KERNEL=0)}.get(path, {})
+    kw = dict(norm=norm, eps=EPS, scaling="mxfp8", fp8="e4m3", layout=layout)
+    with env(**knobs):
+        ref = nf.fwd(x, g, b, **kw)
+        out, call = nf.prepare_fwd(x, g, b, scales_padded=True, **kw)
+        for k in ("scale_inv", "colwise_scale_inv"):
+            if out[k] is not None:
+                out[k].fill_(SENTINEL)
+        call()
+    torch.cuda.synchronize()
+    return case, ref, out
+
+
+@pytest.mark.parametrize("path,layout,norm,rows,hidden", [
+    ("row", "rowwise", "rmsnorm", 130, 1000),
+    ("row", "rowwise", "layernorm", 7, 20480),
+    ("tiles", "rowwise_colwise", "rmsnorm", 300, 4104),
+    ("tiles", "colwise_rowmajor", "layernorm", 200, 1000),
+    ("tiles", "rowwise_colwise_rowmajor", "rmsnorm", 129, 2056),
+    ("band", "rowwise_colwise", "rmsnorm", 70, 1024),
+    ("general", "rowwise_colwise", "rmsnorm", 45, 1001),
+    ("general", "rowwise_colwise_rowmajor", "layernorm", 33, 130),
+])
+def test_fwd_mxfp8_scales_padded(path, layout, norm, rows, hidden):
+    case, ref, out = _padded_case(path, layout, norm, rows, hidden)
+    nb_r, nb_c = (hidden + 31) // 32, (rows + 31) // 32
+    rup = lambda a, m: (a + m - 1) // m * m
+    checks_made = 0
+    for k, logical in (("scale_inv", (rows, nb_r)),
+                       ("colwise_scale_inv", (nb_c, hidden) if layout.endswith("_rowmajor") else (hidden, nb_c))):
+        if ref[k] is None:
+            continue
+        got = out[k].cpu().numpy()
+        blocks_first = k == "colwise_scale_inv" and layout.endswith("_rowmajor")
+        want_shape = ((rup(logical[0], 4), rup(logical[1], 128)) if blocks_first
+                      else (rup(logical[0], 128), rup(logical[1], 4)))
+        assert got.shape == want_shape, (k, got.shape, want_shape)
+        a, c = logical
+        assert np.array_equal(got[:a, :c], ref[k].cpu().numpy()), k
+        pad = np.ones(got.shape, dtype=bool)
+        pad[:a, :c] = False
+        assert np.all(got[pad] == SENTINEL), k
+        checks_made += 1
+    assert checks_made == (2 if "colwise" in layout and layout.startswith("rowwise") else 1)
+    for k in ("y", "y_colwise"):
+        if ref[k] is not None:
+            assert torch.equal(out[k], ref[k]), k
+    # and against the oracle on the logical region
+    if path == "tiles" and layout == "rowwise_colwise":
+        r = oracle_fwd(case, norm, "bf16", "f32", False)
+        checks.check_mx_rows(bits(out["y"]), out["scale_inv"].cpu().numpy()[:rows, :nb_r], r["v"], "e4m3", "mx rowwise")
+        checks.check_mx_rows(bits(out["y_colwise"]), out["colwise_scale_inv"].cpu().numpy()[:hidden, :nb_c],
+                             np.ascontiguousarray(r["v"].T), "e4m3", "mx colwise")
+    assert_ws_clean()
+
+
 @pytest.mark.parametrize("fp8", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("path", ["row", "tiles", "band"])
 @pytest.mark.parametrize("norm,rows,hidden", [("rmsnorm", 300, 4104), ("layernorm", 45, 1000),
