@@ -130,6 +130,7 @@ struct FwdPlan {
   size_t stats_off = 0;  // two-pass path: mu / rsigma when the caller passes none
   bool col_rowmajor = false;
   bool scales_padded = false;  // MXFP8 E8M0 grids padded (block dimension to 4, the other to 128)
+  bool tr = false;    // delayed scaling, rowwise + columnwise: row kernel, then a byte transpose
   bool gen = false;   // general kernels: hidden not a multiple of 8 (or, at launch, unaligned tensors)
 };
 
@@ -196,6 +197,11 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   pl->col = pl->colwise && row_cfg >= 0 && tile_fits && !force_band && env_int("NORMFP8_COL_KERNEL", 1) != 0;
   pl->band = !pl->col && (pl->colwise || row_cfg < 0 || force_band);
   pl->col_rowmajor = col_rowmajor;
+  // delayed scaling with both outputs: the columnwise codes are the rowwise codes transposed
+  // (one scale for the whole tensor), so the row kernel writes the rowwise codes and a byte
+  // transpose reads them back, instead of a statistics pass and a second read of x
+  pl->tr = pl->col && pl->mode == MODE_DELAYED && pl->rowwise && !col_rowmajor && hidden % 16 == 0 &&
+           env_int("NORMFP8_DELAYED_TRANSPOSE", 1) != 0;
   if (pl->gen) {  // the general kernels: rows, then (columnwise) the column pass
     pl->col = pl->band = false;
   } else if (col_rowmajor && !pl->col) {
@@ -512,6 +518,31 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   }
   if (!pl.band && !pl.col) {
     rc = launch_rows(f, pl.mode);
+    if (rc) return rc;
+    return ok();
+  }
+  if (pl.tr) {
+    // rowwise codes, amax, scale_inv and the statistics; then the columnwise codes by transpose
+    rc = launch_rows(f, MODE_DELAYED);
+    if (rc) return rc;
+    TransposeParams t{};
+    t.src = static_cast<const uint8_t *>(y);
+    t.dst = static_cast<uint8_t *>(y_colwise);
+    t.scale = scale;
+    t.col_scale_inv = static_cast<float *>(colwise_scale_inv);
+    t.rows = rows;
+    t.hidden = hidden;
+    t.tiles_r = cdiv(rows, kTrRows);
+    t.tiles_c = cdiv(hidden, kTrCols);
+    const void *fn = transpose_u8_kernel_ptr();
+    int occ = 1;
+    rc = occupancy(fn, kTrThreads, &occ);
+    if (rc) return rc;
+    int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
+    if (cap > kMaxGrid) cap = kMaxGrid;
+    const int64_t tiles = t.tiles_r * t.tiles_c;
+    const int64_t grid = tiles < cap ? tiles : cap;
+    rc = launch(fn, dim3((unsigned)(grid < 1 ? 1 : grid)), dim3(kTrThreads), &t, st);
     if (rc) return rc;
     return ok();
   }

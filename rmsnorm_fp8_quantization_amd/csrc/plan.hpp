@@ -109,6 +109,20 @@ struct FwdTileParams {
   int col_rowmajor;      // columnwise output in the [rows, hidden] layout (scales [rows/32, hidden])
 };
 
+// ---- byte transpose (columnwise codes of delayed per-tensor scaling) ----------------------
+// With one scale for the whole tensor the columnwise codes are the rowwise codes transposed:
+// src [rows, hidden] u8 -> dst [hidden, rows] u8, in tiles of 128 rows x 256 columns.
+struct TransposeParams {
+  const uint8_t *src;
+  uint8_t *dst;
+  const float *scale;    // the tensor scale: colwise_scale_inv = 1 / scale (written once)
+  float *col_scale_inv;  // float32[1]
+  int64_t rows;
+  int64_t hidden;        // a multiple of 16
+  int64_t tiles_r;       // ceil(rows / 128)
+  int64_t tiles_c;       // ceil(hidden / 256)
+};
+
 // ---- backward ------------------------------------------------------------------------------
 // A workgroup of W waves handles one row at a time (all lanes of the workgroup on one row),
 // loops over rows g, g + G, ...; lane owns KC strips (columns 8 * (tid + 64 * W * k)).

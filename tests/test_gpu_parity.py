@@ -218,6 +218,34 @@ def test_fwd_delayed(fp8, layout, norm, rows, hidden):
     assert_ws_clean()
 
 
+@pytest.mark.parametrize("rows,hidden", [(300, 4096), (129, 8192), (37, 2064), (256, 512), (1, 16)])
+def test_fwd_delayed_transpose_path_matches_tiles(rows, hidden):
+    """Delayed scaling with both outputs: the row kernel + byte transpose path gives the same
+    bytes as the statistics + tile path, and both match the oracle."""
+    case = workloads.small_case("rmsnorm", rows, hidden, "bf16", "f32", seed=rows + 11)
+    xh = case["x"].float()
+    xh[::5, ::11] *= 20.0
+    case["x"] = xh.to(torch.bfloat16)
+    ref = oracle_fwd(case, "rmsnorm", "bf16", "f32", False)
+    scale = float(np.float32(448.0) / np.float32(np.max(np.abs(ref["v"])) / 2))
+    x, g = gpu(case, "x", "gamma")
+    outs = []
+    for knob in ("1", "0"):
+        with env(NORMFP8_DELAYED_TRANSPOSE=knob):
+            o = nf.fwd(x, g, None, norm="rmsnorm", eps=EPS, scaling="delayed", fp8="e4m3", layout="rowwise_colwise",
+                       scale=torch.tensor([scale], device="cuda"), amax=torch.zeros(1, device="cuda"))
+        torch.cuda.synchronize()
+        outs.append(o)
+        got = {"y": bits(o["y"]), "y_colwise": bits(o["y_colwise"]), "scale_inv": o["scale_inv"].item(),
+               "colwise_scale_inv": o["colwise_scale_inv"].item(), "amax": o["amax"].item()}
+        checks.check_delayed(got, ref["v"], scale, 0.0, "e4m3", rowwise=True, colwise=True)
+    a, b = outs
+    for k in ("y", "y_colwise", "rsigma", "scale_inv", "colwise_scale_inv", "amax"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a["y_colwise"], a["y"].t().contiguous())
+    assert_ws_clean()
+
+
 def test_fwd_delayed_amax_inplace_and_accumulates():
     case = workloads.small_case("rmsnorm", 16, 512, "bf16", "f32", seed=2)
     ref = oracle_fwd(case, "rmsnorm", "bf16", "f32", False)
