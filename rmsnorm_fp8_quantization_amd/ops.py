@@ -167,7 +167,8 @@ def prepare_fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tenso
 def fwd(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor] = None,
         **kw) -> Dict[str, torch.Tensor]:
     """LayerNorm / RMSNorm forward with an optional FP8 epilogue (one kernel launch; two for a
-    columnwise output: row statistics, then 128 x 128 tiles).
+    columnwise output: row statistics, then 128 x 128 tiles; or, for delayed scaling with both
+    outputs, the rowwise codes, then their transpose).
 
     x: [rows, hidden] (f32/f16/bf16); gamma, beta: [hidden]. Keywords: norm ("layernorm" |
     "rmsnorm"), eps, zero_centered_gamma, scaling ("none" | "delayed" | "mxfp8" | "mxfp8_ceil": MXFP8 with the round-up exponent
