@@ -399,27 +399,34 @@ static const void *pick_tile_in(int in_dtype, int mode, bool crm) {
 // Columnwise codes of delayed per-tensor scaling as a byte transpose of the rowwise codes the
 // row kernel wrote: code(c, r) of the transposed tensor is code(r, c), the same value quantised
 // with the same scale. Reads the 256 MiB of rowwise codes instead of the 512 MiB of input a second
-// time. A workgroup of 8 waves takes tiles of 128 rows x 256 columns: wave w owns rows
-// [16w, 16w + 16), lane l holds rows 16w + 4 (l >> 4) + k (k < 4) of the 16 columns
+// time. A workgroup of 8 waves takes tiles of TR = 32 * RL rows x 256 columns: wave w owns rows
+// [4 RL w, 4 RL (w + 1)), lane l holds RL rows from 4 RL w + RL (l >> 4) of the 16 columns
 // 16 (l % 16) + 0..15 (one 16-byte load per row; one load instruction covers 4 rows x 256 bytes),
 // transposes them in 4 x 4 byte blocks into its 16 columns' 4-row pieces, stages them in LDS as
-// [column][128 rows] (16-byte groups XOR-swizzled as in the tile kernel, two buffers in turn)
-// and stores every column's 128 rows as one 128-byte line (8 lanes x 16 bytes). The next tile is
-// loaded while the current one is transposed.
-__global__ __launch_bounds__(kTrThreads) void transpose_u8_kernel(TransposeParams tp) {
-  static_assert(kTrRows == 128 && kTrCols == 256 && kTrThreads == 512, "tile shape");
+// [column][TR rows] (16-byte groups XOR-swizzled as in the tile kernel) and stores every column's
+// TR rows as whole lines (TR / 16 lanes x 16 bytes). The next tile is loaded while the current
+// one is transposed. RL = 8 (used): 256-row tiles (256-byte column pieces), one staging buffer
+// and a second barrier; RL = 4: 128-row tiles, two staging buffers in turn (slower: the longer
+// column pieces are the cheaper writes).
+template <int RL>
+__global__ __launch_bounds__(kTrThreads) __attribute__((amdgpu_waves_per_eu(4)))  // two workgroups per CU
+void transpose_u8_kernel(TransposeParams tp) {
+  static_assert(kTrCols == 256 && kTrThreads == 512 && (RL == 4 || RL == 8), "tile shape");
+  constexpr int TR = 32 * RL;           // rows per tile
+  constexpr int NBUF = RL == 4 ? 2 : 1;  // staging buffers
+  constexpr int LPC = TR / 16;          // lanes per column line
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int rg = lane >> 4;
   const int cl = lane & 15;
-  const int rloc = 16 * wave + 4 * rg;
+  const int rloc = 4 * RL * wave + RL * rg;
   const int cloc = 16 * cl;
   const int64_t H = tp.hidden;
   const int64_t N = tp.rows;
   const uint32_t ntiles = (uint32_t)(tp.tiles_r * tp.tiles_c);
   const uint32_t tiles_c = (uint32_t)tp.tiles_c;
-  __shared__ __align__(16) uint8_t stage[2][kTrCols * kTrRows];
+  __shared__ __align__(16) uint8_t stage[NBUF][kTrCols * TR];
 
   if (blockIdx.x == 0 && tid == 0 && tp.col_scale_inv) *tp.col_scale_inv = 1.0f / *tp.scale;
 
@@ -431,51 +438,54 @@ __global__ __launch_bounds__(kTrThreads) void transpose_u8_kernel(TransposeParam
     T2 T;
     const uint32_t rt = t / tiles_c;
     const uint32_t ct = t - rt * tiles_c;
-    T.r0 = (int64_t)rt * kTrRows;
+    T.r0 = (int64_t)rt * TR;
     T.c0 = (int64_t)ct * kTrCols;
-    T.rows_here = (int)(N - T.r0 < kTrRows ? N - T.r0 : kTrRows);
+    T.rows_here = (int)(N - T.r0 < TR ? N - T.r0 : TR);
     T.cols_here = (int)(H - T.c0 < kTrCols ? H - T.c0 : kTrCols);
     return T;
   };
   // loads are unconditional: a tile past the end reads tile 0, rows / columns past the end of a
   // tile read its first row / column (hidden is a multiple of 16, so a 16-byte piece that starts
   // inside the row ends inside it)
-  auto load_tile = [&](uint4 (&d)[4], uint32_t t) {
+  auto load_tile = [&](uint4 (&d)[RL], uint32_t t) {
     const T2 T = tile_of(t < ntiles ? t : 0u);
     const uint8_t *b = tp.src + T.r0 * H + T.c0;
     const int64_t co = cloc < T.cols_here ? cloc : 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < RL; ++k) {
       const int64_t r = rloc + k < T.rows_here ? rloc + k : 0;
       d[k] = ld_nt16(b + r * H + co);
     }
   };
   auto soff = [](int col, int piece) {  // 4-row piece `piece` of tile column `col`
-    return col * kTrRows + 4 * (piece ^ (((col >> 3) & 7) << 2));
+    return col * TR + 4 * (piece ^ (((col >> 3) & 7) << 2));
   };
-  auto step = [&](uint4 (&cur)[4], uint32_t t, uint4 (&nxt)[4], uint32_t tn, int par) {
+  auto step = [&](uint4 (&cur)[RL], uint32_t t, uint4 (&nxt)[RL], uint32_t tn, int par) {
     const T2 T = tile_of(t);
     load_tile(nxt, tn);
-    uint8_t *const stg = stage[par];
-    const int piece = 4 * wave + rg;
-    const uint32_t w0[4] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w};
-    const uint32_t w1[4] = {cur[1].x, cur[1].y, cur[1].z, cur[1].w};
-    const uint32_t w2[4] = {cur[2].x, cur[2].y, cur[2].z, cur[2].w};
-    const uint32_t w3[4] = {cur[3].x, cur[3].y, cur[3].z, cur[3].w};
+    uint8_t *const stg = stage[NBUF == 2 ? par : 0];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // columns cloc + 4 j .. + 3
-      uint32_t o[4];
-      transpose4x4b(w0[j], w1[j], w2[j], w3[j], o);
+    for (int h = 0; h < RL / 4; ++h) {  // rows rloc + 4 h .. + 3: one 4-row piece per column
+      const int piece = rloc / 4 + h;
+      const uint32_t w0[4] = {cur[4 * h].x, cur[4 * h].y, cur[4 * h].z, cur[4 * h].w};
+      const uint32_t w1[4] = {cur[4 * h + 1].x, cur[4 * h + 1].y, cur[4 * h + 1].z, cur[4 * h + 1].w};
+      const uint32_t w2[4] = {cur[4 * h + 2].x, cur[4 * h + 2].y, cur[4 * h + 2].z, cur[4 * h + 2].w};
+      const uint32_t w3[4] = {cur[4 * h + 3].x, cur[4 * h + 3].y, cur[4 * h + 3].z, cur[4 * h + 3].w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t *>(stg + soff(cloc + 4 * j + c, piece)) = o[c];
+      for (int j = 0; j < 4; ++j) {  // columns cloc + 4 j .. + 3
+        uint32_t o[4];
+        transpose4x4b(w0[j], w1[j], w2[j], w3[j], o);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t *>(stg + soff(cloc + 4 * j + c, piece)) = o[c];
+      }
     }
     __syncthreads();
-    const bool full = T.rows_here == kTrRows && (N % 16) == 0;
+    const bool full = T.rows_here == TR && (N % 16) == 0;
     uint8_t *const dt = tp.dst + T.c0 * N + T.r0;
-    const int m = tid & 7;
+    const int m = tid % LPC;
 #pragma unroll
-    for (int pass = 0; pass < kTrCols / (kTrThreads / 8); ++pass) {
-      const int c = pass * (kTrThreads / 8) + (tid >> 3);
+    for (int pass = 0; pass < kTrCols / (kTrThreads / LPC); ++pass) {
+      const int c = pass * (kTrThreads / LPC) + tid / LPC;
       if (c < T.cols_here) {
         const uint4 v = *reinterpret_cast<const uint4 *>(stg + soff(c, 4 * m));
         uint8_t *dst = dt + (int64_t)c * N + 16 * m;
@@ -489,10 +499,11 @@ __global__ __launch_bounds__(kTrThreads) void transpose_u8_kernel(TransposeParam
         }
       }
     }
-    // no barrier here: the next tile stages into the other buffer
+    // two buffers: the next tile stages into the other one; one buffer: wait for every read
+    if constexpr (NBUF == 1) __syncthreads();
   };
   const uint32_t G = gridDim.x;
-  uint4 A[4], B[4];
+  uint4 A[RL], B[RL];
   load_tile(A, blockIdx.x);
   for (uint32_t t = blockIdx.x; t < ntiles; t += 2 * G) {
     step(A, t, B, t + G, 0);
@@ -501,7 +512,9 @@ __global__ __launch_bounds__(kTrThreads) void transpose_u8_kernel(TransposeParam
   }
 }
 
-const void *transpose_u8_kernel_ptr() { return (const void *)transpose_u8_kernel; }
+const void *transpose_u8_kernel_ptr(int rows_per_lane) {
+  return rows_per_lane == 8 ? (const void *)transpose_u8_kernel<8> : (const void *)transpose_u8_kernel<4>;
+}
 
 const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor) {
   return norm == NT_LAYERNORM ? pick_tile_in<NT_LAYERNORM>(in_dtype, mode, col_rowmajor)

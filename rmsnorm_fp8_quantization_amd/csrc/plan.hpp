@@ -111,7 +111,7 @@ struct FwdTileParams {
 
 // ---- byte transpose (columnwise codes of delayed per-tensor scaling) ----------------------
 // With one scale for the whole tensor the columnwise codes are the rowwise codes transposed:
-// src [rows, hidden] u8 -> dst [hidden, rows] u8, in tiles of 128 rows x 256 columns.
+// src [rows, hidden] u8 -> dst [hidden, rows] u8, in tiles of 128 (or 256) rows x 256 columns.
 struct TransposeParams {
   const uint8_t *src;
   uint8_t *dst;
@@ -119,7 +119,7 @@ struct TransposeParams {
   float *col_scale_inv;  // float32[1]
   int64_t rows;
   int64_t hidden;        // a multiple of 16
-  int64_t tiles_r;       // ceil(rows / 128)
+  int64_t tiles_r;       // ceil(rows / tile rows)
   int64_t tiles_c;       // ceil(hidden / 256)
 };
 
