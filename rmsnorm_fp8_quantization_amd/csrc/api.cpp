@@ -568,7 +568,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     tp.st_mu = st_mu;
     tp.st_rs = st_rs;
     tp.mx_rows = cdiv(rows, 32);
-      tp.mx_col_ld = col_ld;
+    tp.mx_col_ld = col_ld;
     tp.tiles_r = cdiv(rows, kColTileRows);
     tp.tiles_c = cdiv(hidden, kColTileCols);
     tp.write_row = pl.rowwise ? 1 : 0;

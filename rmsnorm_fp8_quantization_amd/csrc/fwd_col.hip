@@ -75,7 +75,6 @@ __device__ __forceinline__ float rowgroup_max(float v) {
 template <int NORM, class IN, int MODE, bool CRM>
 __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp) {
   static_assert(MODE == MODE_DELAYED || MODE == MODE_MX, "columnwise output is FP8");
-
   const FwdRowParams &p = tp.f;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -313,7 +312,7 @@ __global__ __launch_bounds__(kColThreads) void fwd_tile_kernel(FwdTileParams tp)
       }
     }
     if constexpr (MODE == MODE_MX) {
-      // the tile's (up to) four 32-row block exponents of each column, consecutive bytes
+      // the tile's (up to) kBlk 32-row block exponents of each column, consecutive bytes
       if (tid < T.cols_here) {
         const int nb = (T.rows_here + 31) / 32;
         if constexpr (CRM) {  // [ceil(rows/32), hidden] (row stride mx_col_ld): one 128-byte run per block row

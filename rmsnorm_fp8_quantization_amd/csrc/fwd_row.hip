@@ -23,6 +23,7 @@
 
 namespace nf8 {
 
+// weight lookahead of the long-row layout, in strips (compile-time tuning knob; 2 spills)
 #ifndef NF8_WLA
 #define NF8_WLA 1
 #endif
@@ -104,7 +105,6 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
       }
     }
   }
-  // the 8 weights of strip k (from LDS or registers)
   // WL == 2: strip k's raw weights are loaded ahead of their use and converted where used
   auto weights_raw = [&](int k, W8Raw &rg, W8Raw &rb) {
     uint32_t c = cv[k] ? 8u * (uint32_t)(tl + TEAM * k) : 0u;
@@ -124,6 +124,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
       if constexpr (NORM == NT_LAYERNORM) bk[i] = cv[k] ? bk[i] : 0.0f;
     }
   };
+  // the 8 weights of strip k (from the caches, LDS or registers)
   auto weights = [&](int k, float (&gk)[8], float (&bk)[8]) {
     if constexpr (WL == 2) {
       W8Raw rg, rb;
@@ -173,8 +174,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   };
 
   // software pipeline: the next row's loads are issued before the current row is normalised
-  // (not with WL == 2: the registers hold the weights in flight instead, and two workgroups per
-  // compute unit overlap one's loads with the other's normalisation)
+  // (not with WL == 2: the registers hold the weights in flight instead)
   constexpr bool PF = WL != 2;
   Strip<IN> cur[KC], nxt[PF ? KC : 1];
   int64_t base = (int64_t)blockIdx.x * T;
