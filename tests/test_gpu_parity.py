@@ -193,7 +193,8 @@ def test_fwd_zero_centered_gamma_and_zero_rows():
 @pytest.mark.parametrize("fp8", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("layout", ["rowwise", "rowwise_colwise", "colwise"])
 @pytest.mark.parametrize("norm,rows,hidden", [("rmsnorm", 64, 1024), ("rmsnorm", 45, 4104),
-                                              ("layernorm", 100, 2048), ("rmsnorm", 33, 20480)])
+                                              ("layernorm", 100, 2048), ("rmsnorm", 33, 20480),
+                                              ("layernorm", 50, 4096), ("rmsnorm", 130, 3072)])
 def test_fwd_delayed(fp8, layout, norm, rows, hidden):
     case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=rows)
     xh = case["x"].float()
