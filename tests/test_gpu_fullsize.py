@@ -121,6 +121,8 @@ def test_rms_delayed_e4m3_32768x8192_rowwise_colwise():
     got["amax"] = float(np.max(np.abs(ref["v"])))
     checks.check_delayed(got, ref["v"], scale, 0.0, "e4m3", rowwise=True, colwise=True)
     checks.check_stats(None, out["rsigma"].cpu().numpy(), None, full["rsigma"])
+    # one scale for the whole tensor: every columnwise code is the transposed rowwise code
+    assert torch.equal(out["y_colwise"], out["y"].t().contiguous())
     assert nf.workspace_check() == 0
 
 
