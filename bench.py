@@ -294,6 +294,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for rocprofv3 counter calibration)")
+    ap.add_argument("--workload", choices=sorted(W.WORKLOADS), default=None,
+                    help="only time this workload and print its figures (for rocprofv3 runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the method shards by rows "
@@ -307,6 +309,11 @@ def main():
         copy_calibration()
         return
     import rmsnorm_fp8_quantization_amd as nf
+
+    if args.workload:
+        res = run_workload(W.WORKLOADS[args.workload], nf, args.steps, args.warmup, args.workload == HEADLINE)
+        print(json.dumps({"workload": args.workload, **res}))
+        return
 
     hw = W.WORKLOADS[HEADLINE]
     head = run_workload(hw, nf, args.steps, args.warmup, True)
