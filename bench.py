@@ -53,7 +53,7 @@ def fwd_bytes(w: W.Workload) -> int:
         if w.scaling == "mxfp8":
             b += -(-h // 32) * n + (-(-n // 32) * h if w.colwise else 0)
         else:
-            b += 4 + 4 + 4 + (4 if w.colwise else 0)   # scale, amax in; amax, scale_inv(s) out
+            b += 4 + 4 + 4 + 4 + (4 if w.colwise else 0)   # scale, amax in; updated amax, scale_inv(s) out
     return b
 
 
