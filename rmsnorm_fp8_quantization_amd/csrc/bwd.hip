@@ -300,6 +300,7 @@ static const void *pick_bwd_cfg(int cfg) {
     case BWD_W2_K1_T1: return NF8_BWD(BWD_W2_K1_T1);
     case BWD_W4_K1_T1: return NF8_BWD(BWD_W4_K1_T1);
     case BWD_W4_K2_T1: return NF8_BWD(BWD_W4_K2_T1);
+    case BWD_W8_K3: return NF8_BWD(BWD_W8_K3);
     default: return nullptr;
   }
 #undef NF8_BWD

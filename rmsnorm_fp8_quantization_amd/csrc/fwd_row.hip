@@ -61,7 +61,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   const float n_out = 8.0f * KC - n_in;  // zeroed strip elements
 
   // ---- weights
-  __shared__ float wlds[WL == 1 ? NW * COVER : 1];
+  __shared__ float wlds[WL == 1 && MODE != MODE_STATS ? NW * COVER : 1];  // (statistics: no weights)
   float g[WL ? 1 : KC][8];
   float b[(!WL && NORM == NT_LAYERNORM) ? KC : 1][8];
   if constexpr (WL == 2 || MODE == MODE_STATS) {
@@ -406,6 +406,9 @@ static const void *pick_cfg(int cfg) {
     case ROW_W8_K1: return NF8_ROW(8, 1, 1);
     case ROW_W4T2_K2: return NF8_ROW(4, 2, 2);
     case ROW_W16_K8: return NF8_ROW(16, 1, 8);
+    case ROW_W4T2_K4: return NF8_ROW(4, 2, 4);
+    case ROW_W4T4_K4: return NF8_ROW(4, 4, 4);
+    case ROW_W8T2_K4: return NF8_ROW(8, 2, 4);
     default: return nullptr;
   }
 #undef NF8_ROW

@@ -19,6 +19,9 @@ enum RowCfg : int {
   ROW_W8_K1,
   ROW_W4T2_K2,  // 4 waves per row, 2 rows per workgroup
   ROW_W16_K8,   // 16 waves per row (long rows, weights read from the caches per strip)
+  ROW_W4T2_K4,  // 4 waves per row, 2 / 4 rows per workgroup: the rows share the LDS weights
+  ROW_W4T4_K4,
+  ROW_W8T2_K4,  // 8 waves per row, 2 rows per workgroup
   ROW_NCFG
 };
 struct RowShape {
@@ -27,7 +30,8 @@ struct RowShape {
   int64_t cover() const { return 512LL * P * KC; }  // row elements one team holds
 };
 constexpr RowShape kRowShapes[ROW_NCFG] = {{1, 4, 1}, {1, 4, 2}, {1, 4, 4}, {1, 4, 8}, {4, 1, 2}, {4, 1, 4},
-                                           {8, 1, 4}, {2, 2, 4}, {8, 1, 1}, {4, 2, 2}, {16, 1, 8}};
+                                           {8, 1, 4}, {2, 2, 4}, {8, 1, 1}, {4, 2, 2}, {16, 1, 8},
+                                           {4, 2, 4}, {4, 4, 4}, {8, 2, 4}};
 
 // ---- forward band kernel: 4 waves, RW rows per wave, KC strips per lane
 enum BandCfg : int { BAND_R8_K1 = 0, BAND_R8_K2, BAND_R4_K2, BAND_R1_K4, BAND_R2_K8, BAND_NCFG };
@@ -52,6 +56,7 @@ enum BwdCfg : int {
   BWD_W2_K1_T1,  // one-team twins of the first three, for few rows per workgroup
   BWD_W4_K1_T1,
   BWD_W4_K2_T1,
+  BWD_W8_K3,     // 8 waves x 3 strips: rows up to 12288 with the next row in flight
   BWD_NCFG
 };
 // T teams of W waves per workgroup, each team on its own row; the teams share one partial
@@ -66,7 +71,7 @@ struct BwdShape {
 #endif
 constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1, 4}, {4, 1, 2}, {4, 2, NF8_BWD_T4K2}, {8, 2, 1},
                                            {16, 2, 1}, {8, 1, 1}, {16, 1, 1}, {4, 4, 1},
-                                           {2, 1, 1}, {4, 1, 1}, {4, 2, 1}};
+                                           {2, 1, 1}, {4, 1, 1}, {4, 2, 1}, {8, 3, 1}};
 
 // ---- forward tile kernel (second pass of a columnwise output): 8 waves, 128 x 128 tiles
 #ifndef NF8_COL_TILE_ROWS
