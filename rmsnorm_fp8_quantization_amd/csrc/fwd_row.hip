@@ -406,9 +406,8 @@ static const void *pick_cfg(int cfg) {
     case ROW_W8_K1: return NF8_ROW(8, 1, 1);
     case ROW_W4T2_K2: return NF8_ROW(4, 2, 2);
     case ROW_W16_K8: return NF8_ROW(16, 1, 8);
-    case ROW_W4T2_K4: return NF8_ROW(4, 2, 4);
     case ROW_W4T4_K4: return NF8_ROW(4, 4, 4);
-    case ROW_W8T2_K4: return NF8_ROW(8, 2, 4);
+    case ROW_W16_K2: return NF8_ROW(16, 1, 2);
     default: return nullptr;
   }
 #undef NF8_ROW

@@ -111,7 +111,7 @@ def test_fwd_plain_other_out_dtype_and_bf16_weights(out_dt):
     checks.check_hp(bits(out["y"]), ref["v"], out_dt, terms=ln_terms(case, ref, "layernorm", "bf16"))
 
 
-ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096, 65536, 8192, 8192, 16384]   # per row layout
+ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096, 65536, 8192, 16384]   # per row layout
 BWD_COVER = [1024, 2048, 4096, 8192, 16384, 4096, 8192, 8192, 1024, 2048, 4096, 12288]
 
 
