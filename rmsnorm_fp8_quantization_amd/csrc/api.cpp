@@ -541,12 +541,14 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     t.col_scale_inv = static_cast<float *>(colwise_scale_inv);
     t.rows = rows;
     t.hidden = hidden;
-    // rows per lane: 8 (256-row tiles, 256-byte column pieces: 125 us against 139 us for 128-row
-    // tiles at 32768 x 8192)
-    const int rl = env_int("NORMFP8_TRANSPOSE_RL", 8) == 4 ? 4 : 8;
-    t.tiles_r = cdiv(rows, 32 * rl);
-    t.tiles_c = cdiv(hidden, kTrCols);
-    const void *fn = transpose_u8_kernel_ptr(rl);
+    // tile shape: 512 rows x 128 columns (512-byte column pieces; at 32768 x 8192 the call takes
+    // 260 us against 265 us with 256 x 256 tiles and 279 us with 128 x 256)
+    const int tc = env_int("NORMFP8_TRANSPOSE_TC", 128) == 256 ? 256 : 128;
+    const int rl = tc == 128 || env_int("NORMFP8_TRANSPOSE_RL", 8) != 4 ? 8 : 4;
+    t.tiles_r = cdiv(rows, tc == 128 ? 512 : 32 * rl);
+    t.tiles_c = cdiv(hidden, tc);
+    const void *fn = transpose_u8_kernel_ptr(rl, tc);
+    if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no transpose kernel for this tile shape");
     int occ = 1;
     rc = occupancy(fn, kTrThreads, &occ);
     if (rc) return rc;

@@ -398,34 +398,36 @@ static const void *pick_tile_in(int in_dtype, int mode, bool crm) {
 // Columnwise codes of delayed per-tensor scaling as a byte transpose of the rowwise codes the
 // row kernel wrote: code(c, r) of the transposed tensor is code(r, c), the same value quantised
 // with the same scale. Reads the 256 MiB of rowwise codes instead of the 512 MiB of input a second
-// time. A workgroup of 8 waves takes tiles of TR = 32 * RL rows x 256 columns: wave w owns rows
-// [4 RL w, 4 RL (w + 1)), lane l holds RL rows from 4 RL w + RL (l >> 4) of the 16 columns
-// 16 (l % 16) + 0..15 (one 16-byte load per row; one load instruction covers 4 rows x 256 bytes),
-// transposes them in 4 x 4 byte blocks into its 16 columns' 4-row pieces, stages them in LDS as
-// [column][TR rows] (16-byte groups XOR-swizzled as in the tile kernel) and stores every column's
-// TR rows as whole lines (TR / 16 lanes x 16 bytes). The next tile is loaded while the current
-// one is transposed. RL = 8 (used): 256-row tiles (256-byte column pieces), one staging buffer
-// and a second barrier; RL = 4: 128-row tiles, two staging buffers in turn (slower: the longer
-// column pieces are the cheaper writes).
-template <int RL>
+// time. A workgroup of 8 waves takes tiles of TR rows x TC columns. A lane holds RL rows of 16
+// columns (one 16-byte load per row; TC / 16 lanes cover a tile row, so one load instruction
+// covers 64 * 16 / TC rows), transposes them in 4 x 4 byte blocks into its 16 columns' 4-row
+// pieces, stages them in LDS as [column][TR rows] (16-byte groups XOR-swizzled as in the tile
+// kernel) and stores every column's TR rows as whole lines (TR / 16 lanes x 16 bytes). The next
+// tile is loaded while the current one is transposed. Shapes: 512 x 128 (RL = 8, used: 512-byte
+// column pieces), 256 x 256 (RL = 8) and 128 x 256 (RL = 4, two staging buffers in turn); one
+// staging buffer takes a second barrier. The longer the column pieces, the cheaper the
+// transposed writes.
+template <int RL, int TC>
 __global__ __launch_bounds__(kTrThreads) __attribute__((amdgpu_waves_per_eu(4)))  // two workgroups per CU
 void transpose_u8_kernel(TransposeParams tp) {
-  static_assert(kTrCols == 256 && kTrThreads == 512 && (RL == 4 || RL == 8), "tile shape");
-  constexpr int TR = 32 * RL;           // rows per tile
+  static_assert(kTrThreads == 512 && (RL == 4 || RL == 8) && (TC == 256 || (TC == 128 && RL == 8)), "tile shape");
+  constexpr int LPR = TC / 16;           // lanes per tile row (16 bytes each)
+  constexpr int RG = 64 / LPR;           // row groups per wave
+  constexpr int TR = 8 * RG * RL;        // rows per tile: 8 waves x RG groups x RL rows
   constexpr int NBUF = RL == 4 ? 2 : 1;  // staging buffers
-  constexpr int LPC = TR / 16;          // lanes per column line
+  constexpr int LPC = TR / 16;           // lanes per column line
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rg = lane >> 4;
-  const int cl = lane & 15;
-  const int rloc = 4 * RL * wave + RL * rg;
+  const int rg = lane / LPR;
+  const int cl = lane % LPR;
+  const int rloc = RG * RL * wave + RL * rg;
   const int cloc = 16 * cl;
   const int64_t H = tp.hidden;
   const int64_t N = tp.rows;
   const uint32_t ntiles = (uint32_t)(tp.tiles_r * tp.tiles_c);
   const uint32_t tiles_c = (uint32_t)tp.tiles_c;
-  __shared__ __align__(16) uint8_t stage[NBUF][kTrCols * TR];
+  __shared__ __align__(16) uint8_t stage[NBUF][TC * TR];
 
   if (blockIdx.x == 0 && tid == 0 && tp.col_scale_inv) *tp.col_scale_inv = 1.0f / *tp.scale;
 
@@ -438,9 +440,9 @@ void transpose_u8_kernel(TransposeParams tp) {
     const uint32_t rt = t / tiles_c;
     const uint32_t ct = t - rt * tiles_c;
     T.r0 = (int64_t)rt * TR;
-    T.c0 = (int64_t)ct * kTrCols;
+    T.c0 = (int64_t)ct * TC;
     T.rows_here = (int)(N - T.r0 < TR ? N - T.r0 : TR);
-    T.cols_here = (int)(H - T.c0 < kTrCols ? H - T.c0 : kTrCols);
+    T.cols_here = (int)(H - T.c0 < TC ? H - T.c0 : TC);
     return T;
   };
   // loads are unconditional: a tile past the end reads tile 0, rows / columns past the end of a
@@ -483,7 +485,7 @@ void transpose_u8_kernel(TransposeParams tp) {
     uint8_t *const dt = tp.dst + T.c0 * N + T.r0;
     const int m = tid % LPC;
 #pragma unroll
-    for (int pass = 0; pass < kTrCols / (kTrThreads / LPC); ++pass) {
+    for (int pass = 0; pass < TC / (kTrThreads / LPC); ++pass) {
       const int c = pass * (kTrThreads / LPC) + tid / LPC;
       if (c < T.cols_here) {
         const uint4 v = *reinterpret_cast<const uint4 *>(stg + soff(c, 4 * m));
@@ -511,8 +513,9 @@ void transpose_u8_kernel(TransposeParams tp) {
   }
 }
 
-const void *transpose_u8_kernel_ptr(int rows_per_lane) {
-  return rows_per_lane == 8 ? (const void *)transpose_u8_kernel<8> : (const void *)transpose_u8_kernel<4>;
+const void *transpose_u8_kernel_ptr(int rows_per_lane, int tile_cols) {
+  if (tile_cols == 128) return rows_per_lane == 8 ? (const void *)transpose_u8_kernel<8, 128> : nullptr;
+  return rows_per_lane == 8 ? (const void *)transpose_u8_kernel<8, 256> : (const void *)transpose_u8_kernel<4, 256>;
 }
 
 const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor) {

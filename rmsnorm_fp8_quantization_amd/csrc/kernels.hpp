@@ -83,8 +83,10 @@ constexpr int kColThreads = 4 * kColTileRows;  // 16 rows per wave
 const void *fwd_row_kernel_ptr(int norm, int in_dtype, int mode, int cfg);
 const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg);
 const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor);
-const void *transpose_u8_kernel_ptr(int rows_per_lane);  // 4: 128-row tiles, 8: 256-row tiles
-constexpr int kTrCols = 256, kTrThreads = 512;
+// tiles of 32 * rows_per_lane rows x 256 columns (rows_per_lane 4 or 8), or of 512 rows x 128
+// columns (tile_cols 128, rows_per_lane 8)
+const void *transpose_u8_kernel_ptr(int rows_per_lane, int tile_cols);
+constexpr int kTrThreads = 512;
 // general kernels (any hidden size, element-aligned tensors)
 const void *fwd_gen_row_kernel_ptr(int norm, int in_dtype, int mode);
 const void *fwd_gen_col_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor);

@@ -219,11 +219,13 @@ def test_fwd_delayed(fp8, layout, norm, rows, hidden):
     assert_ws_clean()
 
 
-@pytest.mark.parametrize("rl", ["8", "4"])
-@pytest.mark.parametrize("rows,hidden", [(300, 4096), (129, 8192), (37, 2064), (256, 512), (1, 16), (512, 768)])
-def test_fwd_delayed_transpose_path_matches_tiles(rows, hidden, rl):
-    """Delayed scaling with both outputs: the row kernel + byte transpose path gives the same
-    bytes as the statistics + tile path, and both match the oracle."""
+@pytest.mark.parametrize("rl,tc", [("8", "256"), ("4", "256"), ("8", "128")])
+@pytest.mark.parametrize("rows,hidden", [(300, 4096), (129, 8192), (37, 2064), (256, 512), (1, 16), (512, 768),
+                                         (1100, 400)])
+def test_fwd_delayed_transpose_path_matches_tiles(rows, hidden, rl, tc):
+    """Delayed scaling with both outputs: the row kernel + byte transpose path (each tile
+    shape: 256 or 128 rows x 256 columns, 512 rows x 128 columns) gives the same bytes as the
+    statistics + tile path, and both match the oracle."""
     case = workloads.small_case("rmsnorm", rows, hidden, "bf16", "f32", seed=rows + 11)
     xh = case["x"].float()
     xh[::5, ::11] *= 20.0
@@ -233,7 +235,7 @@ def test_fwd_delayed_transpose_path_matches_tiles(rows, hidden, rl):
     x, g = gpu(case, "x", "gamma")
     outs = []
     for knob in ("1", "0"):
-        with env(NORMFP8_DELAYED_TRANSPOSE=knob, NORMFP8_TRANSPOSE_RL=rl):
+        with env(NORMFP8_DELAYED_TRANSPOSE=knob, NORMFP8_TRANSPOSE_RL=rl, NORMFP8_TRANSPOSE_TC=tc):
             o = nf.fwd(x, g, None, norm="rmsnorm", eps=EPS, scaling="delayed", fp8="e4m3", layout="rowwise_colwise",
                        scale=torch.tensor([scale], device="cuda"), amax=torch.zeros(1, device="cuda"))
         torch.cuda.synchronize()
