@@ -408,6 +408,9 @@ static const void *pick_cfg(int cfg) {
     case ROW_W16_K8: return NF8_ROW(16, 1, 8);
     case ROW_W4T4_K4: return NF8_ROW(4, 4, 4);
     case ROW_W16_K2: return NF8_ROW(16, 1, 2);
+    // weights in LDS whatever their size (LayerNorm: 128 KB for 16384 elements, one workgroup
+    // of 16 waves per CU)
+    case ROW_W8T2_K4: return (const void *)fwd_row_kernel<NORM, IN, MODE, 8, 2, 4, 1>;
     default: return nullptr;
   }
 #undef NF8_ROW

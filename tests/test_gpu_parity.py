@@ -111,7 +111,7 @@ def test_fwd_plain_other_out_dtype_and_bf16_weights(out_dt):
     checks.check_hp(bits(out["y"]), ref["v"], out_dt, terms=ln_terms(case, ref, "layernorm", "bf16"))
 
 
-ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096, 65536, 8192, 16384]   # per row layout
+ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096, 65536, 8192, 16384, 16384]   # per row layout
 BWD_COVER = [1024, 2048, 4096, 8192, 16384, 4096, 8192, 8192, 1024, 2048, 4096, 12288]
 
 
@@ -131,15 +131,16 @@ def test_fwd_every_row_layout(cfg, norm):
 
 
 # rows longer than 16384 elements: the 16-wave layout whose weights are read from the caches a
-# strip ahead of their use; RMSNorm rows of 8193..16384 elements, whose FP8 epilogues run on
-# 8 waves x 4 strips and plain outputs on 16 waves x 2 strips (any weight dtype, zero-centred
-# gamma, every rowwise epilogue)
+# strip ahead of their use; rows of 8193..16384 elements: RMSNorm FP8 epilogues on 8 waves x
+# 4 strips, its plain outputs on 16 waves x 2 strips, LayerNorm on two 8-wave rows per
+# workgroup sharing the LDS weights (any weight dtype, zero-centred gamma, every rowwise epilogue)
 @pytest.mark.parametrize("w_dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("mode", ["none", "delayed", "mxfp8"])
 @pytest.mark.parametrize("norm,hidden,zc", [("layernorm", 65536, False), ("rmsnorm", 65536, True),
                                             ("layernorm", 40000, True), ("rmsnorm", 20488, False),
                                             ("rmsnorm", 12288, True), ("rmsnorm", 10232, False),
-                                            ("rmsnorm", 16384, False)])
+                                            ("rmsnorm", 16384, False), ("layernorm", 12288, True),
+                                            ("layernorm", 10232, False)])
 def test_fwd_long_rows(w_dt, mode, norm, hidden, zc):
     rows = 5
     case = workloads.small_case(norm, rows, hidden, "bf16", w_dt, seed=hidden % 97 + rows, zero_centered_gamma=zc)
