@@ -442,11 +442,32 @@ __device__ __forceinline__ void publish_amax(uint32_t *ws, float a, uint32_t tag
   st_dev64(reinterpret_cast<uint64_t *>(ws + kWsAmax0) + blockIdx.x, tagged(a, tag));
 }
 
-// max over the per-workgroup amax entries [0, n) (all threads of the last workgroup)
+// max over the per-workgroup amax entries [0, n) (all threads of the last workgroup). Each
+// thread loads a batch of 8 entries before it looks at any of them, so a launch with a few
+// thousand workgroups costs one round trip rather than one per entry; only an entry whose tag
+// is not yet this launch's is polled again.
 __device__ __forceinline__ float gather_amax(uint32_t *ws, int n, float *lds_red, uint32_t tag) {
+  constexpr int B = 8;
   const uint64_t *parts = reinterpret_cast<const uint64_t *>(ws + kWsAmax0);
+  const int nt = (int)blockDim.x;
   float a = 0.0f;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) a = fmaxf(a, wait_tagged(parts + i, tag, ws + kWsError));
+  for (int i0 = (int)threadIdx.x; i0 < n; i0 += B * nt) {
+    uint64_t v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = i0 + j * nt;
+      v[j] = ld_dev64(parts + (i < n ? i : 0));  // (an index past the end reloads entry 0, unused)
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = i0 + j * nt;
+      if (i < n) {
+        const float x = (uint32_t)(v[j] >> 32) == tag ? __uint_as_float((uint32_t)v[j])
+                                                       : wait_tagged(parts + i, tag, ws + kWsError);
+        a = fmaxf(a, x);
+      }
+    }
+  }
   a = wave_max(a);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) lds_red[w] = a;

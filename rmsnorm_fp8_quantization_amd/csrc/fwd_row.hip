@@ -151,11 +151,13 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   };
 
   float scale = 1.0f;
-  uint32_t tag = 0;
+  // launch epoch (thread 0): loaded here, first needed when the workgroup publishes its amax,
+  // so nothing waits for it before the first row's loads go out
+  uint32_t epoch = 0;
   __shared__ uint32_t s_epoch;
   if constexpr (MODE == MODE_DELAYED) {
     scale = *p.scale;
-    tag = epoch_tag(read_epoch(p.ws, &s_epoch));
+    if (tid == 0) epoch = ld_dev_u32(p.ws + kWsEpoch);
   }
   float amax_local = 0.0f;
 
@@ -369,12 +371,13 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
       float a = wred[0];
 #pragma unroll
       for (int w = 1; w < P * T; ++w) a = fmaxf(a, wred[w]);
-      publish_amax(p.ws, a, tag);
+      s_epoch = epoch;  // for the last workgroup's gather (visible after finish_workgroup's barrier)
+      publish_amax(p.ws, a, epoch_tag(epoch));
       if (blockIdx.x == 0) *static_cast<float *>(p.scale_inv) = 1.0f / scale;
     }
     vmem_drain();
     if (finish_workgroup(p.ws, &last_flag)) {
-      const float tot = gather_amax(p.ws, gridDim.x, wred, tag);
+      const float tot = gather_amax(p.ws, gridDim.x, wred, epoch_tag(s_epoch));
       if (tid == 0) *p.updated_amax = fmaxf(*p.amax_in, tot);
       reset_completion(p.ws);
     }
