@@ -213,13 +213,16 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   // transpose reads them back, instead of a statistics pass and a second read of x
   pl->tr = pl->col && pl->mode == MODE_DELAYED && pl->rowwise && !col_rowmajor && hidden % 16 == 0 &&
            env_int("NORMFP8_DELAYED_TRANSPOSE", 1) != 0;
-  // RMSNorm rows of 8193..16384 elements whose row kernel writes FP8 codes (the rowwise path and
-  // the transpose route, not the statistics pass): 8 waves x 4 strips (16384 x 12288: delayed
-  // 126 -> 113 us, MXFP8 130 -> 111 us; x 10240: 132 -> 111, 122 -> 101 us; equal at 16384);
-  // with a 2-byte output 16 waves x 2 strips stays faster
-  if (norm_type == NORM_RMSNORM && row_cfg == ROW_W16_K2 && row_override < 0 && pl->mode != MODE_PLAIN &&
-      (!pl->col || pl->tr))
-    row_cfg = ROW_W8_K4;
+  // RMSNorm FP8 rowwise outputs: rows of 8193..16384 elements on 8 waves x 4 strips (16384 x
+  // 12288: delayed 126 -> 113 us, MXFP8 130 -> 111 us; x 10240: 132 -> 111, 122 -> 101 us;
+  // equal at 16384), rows of 2049..4096 on 4 waves x 2 rows x 2 strips (16384 x 4096: delayed
+  // 43-45 -> 39 us, MXFP8 39 -> 36.5 us); with a 2-byte output the defaults stay faster. A
+  // columnwise request keeps the default layout: its transpose route and its statistics + tile
+  // route then reduce every row in the same order and give the same bytes.
+  if (norm_type == NORM_RMSNORM && row_override < 0 && pl->mode != MODE_PLAIN && !pl->col) {
+    if (row_cfg == ROW_W16_K2) row_cfg = ROW_W8_K4;
+    else if (row_cfg == ROW_W2T2_K4) row_cfg = ROW_W4T2_K2;
+  }
   if (pl->gen) {  // the general kernels: rows, then (columnwise) the column pass
     pl->col = pl->band = false;
   } else if (col_rowmajor && !pl->col) {

@@ -133,14 +133,16 @@ def test_fwd_every_row_layout(cfg, norm):
 # rows longer than 16384 elements: the 16-wave layout whose weights are read from the caches a
 # strip ahead of their use; rows of 8193..16384 elements: RMSNorm FP8 epilogues on 8 waves x
 # 4 strips, its plain outputs on 16 waves x 2 strips, LayerNorm on two 8-wave rows per
-# workgroup sharing the LDS weights (any weight dtype, zero-centred gamma, every rowwise epilogue)
+# workgroup sharing the LDS weights; RMSNorm FP8 rowwise epilogues at 2049..4096 elements on
+# 4 waves x 2 rows x 2 strips (any weight dtype, zero-centred gamma, every rowwise epilogue)
 @pytest.mark.parametrize("w_dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("mode", ["none", "delayed", "mxfp8"])
 @pytest.mark.parametrize("norm,hidden,zc", [("layernorm", 65536, False), ("rmsnorm", 65536, True),
                                             ("layernorm", 40000, True), ("rmsnorm", 20488, False),
                                             ("rmsnorm", 12288, True), ("rmsnorm", 10232, False),
                                             ("rmsnorm", 16384, False), ("layernorm", 12288, True),
-                                            ("layernorm", 10232, False)])
+                                            ("layernorm", 10232, False), ("rmsnorm", 4096, True),
+                                            ("rmsnorm", 2056, False)])
 def test_fwd_long_rows(w_dt, mode, norm, hidden, zc):
     rows = 5
     case = workloads.small_case(norm, rows, hidden, "bf16", w_dt, seed=hidden % 97 + rows, zero_centered_gamma=zc)
@@ -226,7 +228,7 @@ def test_fwd_delayed(fp8, layout, norm, rows, hidden):
 
 @pytest.mark.parametrize("rl,tc", [("8", "256"), ("4", "256"), ("8", "128")])
 @pytest.mark.parametrize("rows,hidden", [(300, 4096), (129, 8192), (37, 2064), (256, 512), (1, 16), (512, 768),
-                                         (1100, 400)])
+                                         (1100, 400), (64, 12288)])
 def test_fwd_delayed_transpose_path_matches_tiles(rows, hidden, rl, tc):
     """Delayed scaling with both outputs: the row kernel + byte transpose path (each tile
     shape: 256 or 128 rows x 256 columns, 512 rows x 128 columns) gives the same bytes as the
