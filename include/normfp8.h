@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define NORMFP8_ABI_VERSION 1
+#define NORMFP8_ABI_VERSION 2
 #define NORM_WS_HEADER_BYTES 16384
 
 typedef enum {
@@ -205,6 +205,35 @@ int norm_workspace_init(void *stream, void *workspace, size_t workspace_bytes);
  * clears it. Not for the hot path.
  */
 int norm_workspace_check(void *stream, void *workspace, uint32_t *flags);
+
+/*
+ * Planner query, host only (no GPU needed): the launch shape norm_bwd / norm_bwd_add choose for
+ * these arguments on a device with `cu_count` compute units, `cu_margin` of them left free,
+ * when the backward row kernel fits `occupancy` workgroups per CU. On return shape[0] = layout
+ * index (-1: the general kernels, the rest 0), shape[1] = waves per row team (W), shape[2] =
+ * 16-byte strips per lane (KC), shape[3] = row teams per workgroup (T), shape[4] = workgroups in
+ * the persistent grid (G). Workgroup b's team t visits rows b*T + t + j*G*T, j >= 0, for as long
+ * as b*T + j*G*T < rows, and stores dx only for rows < rows. [NVRTC-PR] Flowchart (grid sizes
+ * from occupancy and the SM margin). For tests that replay the kernel's row walk on the CPU.
+ */
+int norm_bwd_launch_shape(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_type, int with_add,
+                          int cu_count, int cu_margin, int occupancy, int64_t shape[5]);
+
+/*
+ * Tuning and test hook: sets one planner override for the whole process and returns the old
+ * value in *previous (may be NULL). Each override starts from the environment variable of the
+ * same name, read once when the library is first used; INT_MIN means "not set" (the planner's
+ * default). Names: NORMFP8_ROW_CFG, NORMFP8_BAND_CFG, NORMFP8_BWD_CFG (force a kernel shape,
+ * by its index in the library's shape tables), NORMFP8_FORCE_BAND (1: band kernel),
+ * NORMFP8_COL_KERNEL (0: single-pass band kernel for columnwise output),
+ * NORMFP8_DELAYED_TRANSPOSE (0: statistics + tile route for delayed scaling with both
+ * outputs), NORMFP8_TRANSPOSE_TC / NORMFP8_TRANSPOSE_RL (byte-transpose tile shape),
+ * NORMFP8_ROW_OCC (cap on row-kernel workgroups per CU), NORMFP8_ROW_BALANCE (0: plain
+ * occupancy grid), NORMFP8_BAND_CLASSES (1: one ticket class). Unknown names give
+ * NORM_ERR_INVALID_ARG. Not for the hot path of an application: a change affects every later
+ * call in the process.
+ */
+int norm_tuning_set(const char *name, int value, int *previous);
 
 /* Message describing the last error returned on the calling thread ("" if none). */
 const char *norm_last_error(void);

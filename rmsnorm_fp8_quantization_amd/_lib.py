@@ -6,6 +6,7 @@ fallback implementation.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -24,8 +25,10 @@ NORM_Q_SCALES_PADDED = 8
 NORM_WS_HEADER_BYTES = 16384
 
 EXPORTS = ("norm_fwd_workspace_size", "norm_bwd_workspace_size", "norm_fwd", "norm_bwd",
-           "norm_bwd_add", "norm_workspace_init", "norm_workspace_check", "norm_last_error",
-           "norm_abi_version")
+           "norm_bwd_add", "norm_workspace_init", "norm_workspace_check", "norm_bwd_launch_shape",
+           "norm_tuning_set", "norm_last_error", "norm_abi_version")
+ABI_VERSION = 2
+KNOB_UNSET = -2 ** 31  # INT_MIN: a tuning override that is not set
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -42,6 +45,8 @@ _SIGS = {
     "norm_bwd_add": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I, _I, _I, _I],
     "norm_workspace_init": [_P, _P, _SZ],
     "norm_workspace_check": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
+    "norm_bwd_launch_shape": [_I64, _I64, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I64)],
+    "norm_tuning_set": [ctypes.c_char_p, _I, ctypes.POINTER(_I)],
     "norm_last_error": [],
     "norm_abi_version": [],
 }
@@ -83,6 +88,22 @@ def call(name, *args):
     if rc != NORM_OK:
         raise NormError(name, rc, lib.norm_last_error().decode())
     return rc
+
+
+@contextlib.contextmanager
+def tuning(**knobs):
+    """Set planner overrides (``NORMFP8_ROW_CFG=3``, ...) for the duration of a block, through
+    ``norm_tuning_set``, and restore the previous values afterwards."""
+    prev = {}
+    try:
+        for name, value in knobs.items():
+            old = _I(0)
+            call("norm_tuning_set", name.encode(), int(value), ctypes.byref(old))
+            prev[name] = old.value
+        yield
+    finally:
+        for name, value in prev.items():
+            call("norm_tuning_set", name.encode(), value, None)
 
 
 def status(name, *args):

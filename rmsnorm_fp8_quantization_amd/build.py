@@ -30,6 +30,8 @@ def hipcc() -> str:
 
 def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
+            # a local that shadows another (e.g. an array hiding a bool guard) is an error
+            "-Wshadow", "-Werror=shadow", "-Werror=pointer-bool-conversion",
             # never emit packed fp32 VALU ops (v_pk_*_f32)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", CSRC]

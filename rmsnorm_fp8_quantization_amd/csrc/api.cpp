@@ -16,6 +16,8 @@
 // reads device memory and never allocates.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -56,11 +58,45 @@ bool is_fp8(int dt) { return dt == DT_E4M3 || dt == DT_E5M2; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
-// optional integer override from the environment (planner testing / tuning knob)
-int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  if (!v || !*v) return dflt;
-  return atoi(v);
+// ---------------------------------------------------------------- tuning knobs
+// Planner overrides for testing and tuning. Each starts from the process environment, read once
+// (on the library's first use); afterwards only norm_tuning_set changes them. A launch reads
+// them with one relaxed atomic load each.
+constexpr int kKnobUnset = INT_MIN;
+const char *const kKnobNames[] = {"NORMFP8_FORCE_BAND",       "NORMFP8_ROW_CFG",      "NORMFP8_COL_KERNEL",
+                                  "NORMFP8_DELAYED_TRANSPOSE", "NORMFP8_BAND_CFG",     "NORMFP8_BWD_CFG",
+                                  "NORMFP8_ROW_OCC",           "NORMFP8_ROW_BALANCE",  "NORMFP8_TRANSPOSE_TC",
+                                  "NORMFP8_TRANSPOSE_RL",      "NORMFP8_BAND_CLASSES"};
+enum Knob : int {
+  K_FORCE_BAND = 0,
+  K_ROW_CFG,
+  K_COL_KERNEL,
+  K_DELAYED_TRANSPOSE,
+  K_BAND_CFG,
+  K_BWD_CFG,
+  K_ROW_OCC,
+  K_ROW_BALANCE,
+  K_TRANSPOSE_TC,
+  K_TRANSPOSE_RL,
+  K_BAND_CLASSES,
+  K_NKNOBS
+};
+static_assert(sizeof(kKnobNames) / sizeof(kKnobNames[0]) == K_NKNOBS, "knob table");
+std::atomic<int> g_knobs[K_NKNOBS];
+std::once_flag g_knobs_once;
+
+void knobs_init() {
+  std::call_once(g_knobs_once, [] {
+    for (int i = 0; i < K_NKNOBS; ++i) {
+      const char *v = getenv(kKnobNames[i]);
+      g_knobs[i].store(v && *v ? atoi(v) : kKnobUnset, std::memory_order_relaxed);
+    }
+  });
+}
+int knob(Knob k, int dflt) {
+  knobs_init();
+  const int v = g_knobs[k].load(std::memory_order_relaxed);
+  return v == kKnobUnset ? dflt : v;
 }
 
 // ---------------------------------------------------------------- device facts (cached)
@@ -176,9 +212,9 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   pl->colwise = (qlayout & NORM_Q_COLWISE) != 0;
 
   // layout choice
-  const int force_band = env_int("NORMFP8_FORCE_BAND", 0);
+  const int force_band = knob(K_FORCE_BAND, 0);
   int row_cfg = -1;
-  const int row_override = env_int("NORMFP8_ROW_CFG", -1);
+  const int row_override = knob(K_ROW_CFG, -1);
   if (row_override >= 0 && row_override < ROW_NCFG && kRowShapes[row_override].cover() >= hidden) {
     row_cfg = row_override;
   } else {
@@ -205,14 +241,14 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   // (the tile kernel's lane offsets are 32-bit: 128 rows of float32 input, 128 columns of the
   // transposed output)
   const bool tile_fits = (int64_t)hidden * 4 * kColTileRows < (1ll << 32) && rows * kColTileCols < (1ll << 32);
-  pl->col = pl->colwise && row_cfg >= 0 && tile_fits && !force_band && env_int("NORMFP8_COL_KERNEL", 1) != 0;
+  pl->col = pl->colwise && row_cfg >= 0 && tile_fits && !force_band && knob(K_COL_KERNEL, 1) != 0;
   pl->band = !pl->col && (pl->colwise || row_cfg < 0 || force_band);
   pl->col_rowmajor = col_rowmajor;
   // delayed scaling with both outputs: the columnwise codes are the rowwise codes transposed
   // (one scale for the whole tensor), so the row kernel writes the rowwise codes and a byte
   // transpose reads them back, instead of a statistics pass and a second read of x
   pl->tr = pl->col && pl->mode == MODE_DELAYED && pl->rowwise && !col_rowmajor && hidden % 16 == 0 &&
-           env_int("NORMFP8_DELAYED_TRANSPOSE", 1) != 0;
+           knob(K_DELAYED_TRANSPOSE, 1) != 0;
   // RMSNorm FP8 rowwise outputs: rows of 8193..16384 elements on 8 waves x 4 strips (16384 x
   // 12288: delayed 126 -> 113 us, MXFP8 130 -> 111 us; x 10240: 132 -> 111, 122 -> 101 us;
   // equal at 16384), rows of 2049..4096 on 4 waves x 2 rows x 2 strips (16384 x 4096: delayed
@@ -237,7 +273,7 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     int bc;
     if (pl->colwise) bc = hidden <= 512 ? BAND_R8_K1 : BAND_R8_K2;
     else bc = hidden <= 2048 ? BAND_R1_K4 : BAND_R2_K8;
-    const int band_override = env_int("NORMFP8_BAND_CFG", -1);
+    const int band_override = knob(K_BAND_CFG, -1);
     if (band_override >= 0 && band_override < BAND_NCFG &&
         (kBandShapes[band_override].colwise_ok || !pl->colwise) &&
         !(pl->colwise && pl->mode == MODE_MX && kBandShapes[band_override].RW != 8))
@@ -297,7 +333,7 @@ int plan_bwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_t
   if (cu_margin < 0) return fail(NORM_ERR_INVALID_ARG, "cu_margin must be >= 0");
   if (hidden > (int64_t)1 << 24) return fail(NORM_ERR_UNSUPPORTED, "hidden above 2^24 not supported");
   int cfg = -1;
-  const int ov = env_int("NORMFP8_BWD_CFG", -1);
+  const int ov = knob(K_BWD_CFG, -1);
   if (ov >= 0 && ov < BWD_NCFG && kBwdShapes[ov].cover() >= hidden) {
     cfg = ov;
   } else {
@@ -330,6 +366,19 @@ int plan_bwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_t
   if (pl->G_max < kGenChunks) pl->G_max = kGenChunks;
   pl->ws_bytes = kWsHeaderBytes + round_up((size_t)pl->G_max * round_up((size_t)hidden, 32) * arrays * sizeof(float), 256);
   return NORM_OK;
+}
+
+// Persistent grid of the backward row kernel: one workgroup per CU (more for small layouts),
+// capped by the workspace's partial rows and by the row count in units of the layout's T teams,
+// so that every workgroup's first base row b * T is a row of the tensor.
+int64_t bwd_grid(const BwdPlan &pl, int cus_free, int occ, int64_t rows) {
+  const int per_cu = bwd_wgs_per_cu(pl.cfg);
+  int64_t G = (int64_t)cus_free * (occ < per_cu ? occ : per_cu);
+  if (G > pl.G_max) G = pl.G_max;
+  const int64_t slots = cdiv(rows, kBwdShapes[pl.cfg].T);
+  if (G > slots) G = slots;
+  if (G < 1) G = 1;
+  return G;
 }
 
 bool aligned_to(const void *p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -476,7 +525,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     int occ = 1;
     int r = occupancy(fn, sh.threads(), &occ);
     if (r) return r;
-    const int occ_cap = env_int("NORMFP8_ROW_OCC", 0);  // tuning: fewer workgroups per CU
+    const int occ_cap = knob(K_ROW_OCC, 0);  // tuning: fewer workgroups per CU
     if (occ_cap > 0 && occ_cap < occ) occ = occ_cap;
     const int64_t slots = cdiv(rows, sh.T);
     int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
@@ -485,7 +534,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     // the last round does not run on a fraction of the grid
     const int64_t rounds = cdiv(slots, cap < 1 ? 1 : cap);
     int64_t grid = cdiv(slots, rounds < 1 ? 1 : rounds);
-    if (env_int("NORMFP8_ROW_BALANCE", 1) == 0) grid = slots < cap ? slots : cap;
+    if (knob(K_ROW_BALANCE, 1) == 0) grid = slots < cap ? slots : cap;
     if (grid < 1) grid = 1;
     FwdRowParams copy = rp;
     return launch(fn, dim3((unsigned)grid), dim3(sh.threads()), &copy, st);
@@ -555,8 +604,8 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     t.hidden = hidden;
     // tile shape: 512 rows x 128 columns (512-byte column pieces; at 32768 x 8192 the call takes
     // 260 us against 265 us with 256 x 256 tiles and 279 us with 128 x 256)
-    const int tc = env_int("NORMFP8_TRANSPOSE_TC", 128) == 256 ? 256 : 128;
-    const int rl = tc == 128 || env_int("NORMFP8_TRANSPOSE_RL", 8) != 4 ? 8 : 4;
+    const int tc = knob(K_TRANSPOSE_TC, 128) == 256 ? 256 : 128;
+    const int rl = tc == 128 || knob(K_TRANSPOSE_RL, 8) != 4 ? 8 : 4;
     t.tiles_r = cdiv(rows, tc == 128 ? 512 : 32 * rl);
     t.tiles_c = cdiv(hidden, tc);
     const void *fn = transpose_u8_kernel_ptr(rl, tc);
@@ -638,7 +687,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   // ticket classes: one per XCD when every class gets several bands and at least 2S workgroups
   b.classes = 1;
   if (grid >= (int64_t)kClasses * 2 * pl.S && pl.bands >= (int64_t)kClasses * 4 &&
-      env_int("NORMFP8_BAND_CLASSES", kClasses) == kClasses) {
+      knob(K_BAND_CLASSES, kClasses) == kClasses) {
     b.classes = kClasses;
     grid = grid / kClasses * kClasses;
   }
@@ -735,10 +784,7 @@ static int bwd_common(void *stream, bool with_add, const void *dy, const void *x
   int occ = 1;
   rc = occupancy(fn, sh.threads(), &occ);
   if (rc) return rc;
-  int64_t G = (int64_t)(dev.cus - cu_margin) * (occ < bwd_wgs_per_cu(pl.cfg) ? occ : bwd_wgs_per_cu(pl.cfg));
-  if (G > pl.G_max) G = pl.G_max;
-  if (G > rows) G = rows;
-  if (G < 1) G = 1;
+  const int64_t G = bwd_grid(pl, dev.cus - cu_margin, occ, rows);
 
   BwdParams p{};
   p.dy = dy;
@@ -787,6 +833,43 @@ int norm_bwd_add(void *stream, const void *dy, const void *x, const void *residu
   return bwd_common(stream, true, dy, x, residual_dy, nullptr, rsigma, gamma, dx, dgamma, nullptr, workspace,
                     workspace_bytes, rows, hidden, in_dtype, w_dtype, NORM_RMSNORM, zero_centered_gamma,
                     cu_margin);
+}
+
+int norm_bwd_launch_shape(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_type, int with_add,
+                          int cu_count, int cu_margin, int occupancy, int64_t shape[5]) {
+  if (!shape) return fail(NORM_ERR_INVALID_ARG, "shape is NULL");
+  if (with_add && norm_type != NORM_RMSNORM)
+    return fail(NORM_ERR_INVALID_ARG, "the fused backward-add is defined for RMSNorm only");
+  if (cu_count < 1 || cu_margin < 0 || cu_margin >= cu_count || occupancy < 1)
+    return fail(NORM_ERR_INVALID_ARG, "need 0 <= cu_margin < cu_count and occupancy >= 1");
+  BwdPlan pl;
+  int rc = plan_bwd(rows, hidden, in_dtype, w_dtype, norm_type, cu_margin, &pl);
+  if (rc) return rc;
+  if (pl.gen) {
+    shape[0] = -1;
+    shape[1] = shape[2] = shape[3] = shape[4] = 0;
+    return ok();
+  }
+  const BwdShape &sh = kBwdShapes[pl.cfg];
+  shape[0] = pl.cfg;
+  shape[1] = sh.W;
+  shape[2] = sh.KC;
+  shape[3] = sh.T;
+  shape[4] = bwd_grid(pl, cu_count - cu_margin, occupancy, rows);
+  return ok();
+}
+
+int norm_tuning_set(const char *name, int value, int *previous) {
+  if (!name) return fail(NORM_ERR_INVALID_ARG, "name is NULL");
+  knobs_init();
+  for (int i = 0; i < K_NKNOBS; ++i) {
+    if (strcmp(name, kKnobNames[i]) == 0) {
+      const int old = g_knobs[i].exchange(value, std::memory_order_relaxed);
+      if (previous) *previous = old;
+      return ok();
+    }
+  }
+  return fail(NORM_ERR_INVALID_ARG, "unknown tuning knob %s", name);
 }
 
 int norm_workspace_init(void *stream, void *workspace, size_t workspace_bytes) {

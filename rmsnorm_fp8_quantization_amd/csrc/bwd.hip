@@ -134,14 +134,14 @@ __global__ __launch_bounds__(64 * W * T) void bwd_kernel(BwdParams p) {
       float dv[8], xv[8], out[8];
       strip_to_f32<IN>(dys[k], dv);
       strip_to_f32<IN>(xs[k], xv);
-      float rv[8];
-      if constexpr (ADD) strip_to_f32<IN>(rsd[k], rv);
+      float res[8];
+      if constexpr (ADD) strip_to_f32<IN>(rsd[k], res);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float xh = (xv[i] - mu) * rs;
         const float w = dv[i] * g[k][i];
         float d = rs * (w - fmaf(xh, c2, c1));
-        if constexpr (ADD) d += rv[i];
+        if constexpr (ADD) d += res[i];
         out[i] = d;
         dg[k][i] = fmaf(dv[i], xh, dg[k][i]);
         if constexpr (NORM == NT_LAYERNORM) db[k][i] += dv[i];

@@ -28,8 +28,8 @@
 // (two buffers, used in turn) as [column][128 rows] with 16-byte groups XOR-swizzled across
 // banks, and stored so that 8 consecutive lanes write a column's 128-byte line. An MXFP8
 // columnwise block (32 rows) is two waves: each wave reduces its 16 rows per column and the
-// pair combine through LDS. (The tile height is NF8_COL_TILE_ROWS, 128 by default; 256 builds a
-// 16-wave variant whose columns are 256-byte pieces, which measured slower: one workgroup per
+// pair combine through LDS. (The tile height kColTileRows is 128; a 256-row
+// 16-wave variant whose columns are 256-byte pieces measured slower: one workgroup per
 // CU instead of two.)
 #include "device_common.hpp"
 #include "kernels.hpp"

@@ -23,10 +23,8 @@
 
 namespace nf8 {
 
-// weight lookahead of the long-row layout, in strips (compile-time tuning knob; 2 spills)
-#ifndef NF8_WLA
-#define NF8_WLA 1
-#endif
+// weight lookahead of the long-row layout, in strips (2 spills registers)
+constexpr int kWeightLookahead = 1;
 
 // WL: where the weights live while the workgroup walks its rows. 0: each lane keeps its
 // columns' gamma / beta in registers; 1: the workgroup stages them once in LDS (as float32,
@@ -193,7 +191,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
     // WL == 2: the weights of strip k are loaded WLA strips ahead of their use (WLA + 1
     // buffers in turn); the first ones go out before the statistics so their latency hides
     // behind them
-    constexpr int WLA = NF8_WLA;
+    constexpr int WLA = kWeightLookahead;
     constexpr int WQ = WL == 2 && MODE != MODE_STATS ? WLA + 1 : 1;
     W8Raw wq_g[WQ], wq_b[WQ];
     if constexpr (WQ > 1) {

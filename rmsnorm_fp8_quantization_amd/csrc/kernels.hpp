@@ -66,18 +66,14 @@ struct BwdShape {
   constexpr int threads() const { return 64 * W * T; }
   constexpr int64_t cover() const { return 512LL * W * KC; }
 };
-#ifndef NF8_BWD_T4K2
-#define NF8_BWD_T4K2 2
-#endif
-constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1, 4}, {4, 1, 2}, {4, 2, NF8_BWD_T4K2}, {8, 2, 1},
+// (shape constants are fixed here, not overridable per translation unit: the planner in api.cpp
+// and the kernels must agree on every team count, thread count and tile size)
+constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1, 4}, {4, 1, 2}, {4, 2, 2}, {8, 2, 1},
                                            {16, 2, 1}, {8, 1, 1}, {16, 1, 1}, {4, 4, 1},
                                            {2, 1, 1}, {4, 1, 1}, {4, 2, 1}, {8, 3, 1}};
 
 // ---- forward tile kernel (second pass of a columnwise output): 8 waves, 128 x 128 tiles
-#ifndef NF8_COL_TILE_ROWS
-#define NF8_COL_TILE_ROWS 128
-#endif
-constexpr int kColTileRows = NF8_COL_TILE_ROWS;
+constexpr int kColTileRows = 128;
 constexpr int kColTileCols = 128;
 constexpr int kColThreads = 4 * kColTileRows;  // 16 rows per wave
 

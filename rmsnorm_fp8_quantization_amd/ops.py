@@ -32,6 +32,9 @@ _LAYOUT = {"rowwise": L.NORM_Q_ROWWISE, "colwise": L.NORM_Q_COLWISE,
            "rowwise_colwise_rowmajor": L.NORM_Q_ROWWISE_COLWISE | L.NORM_Q_COLWISE_ROWMAJOR}
 
 _ws_cache: Dict[tuple, torch.Tensor] = {}
+# workspaces replaced by larger ones: kept, never freed, because a prepared call or a captured
+# graph may still point at them (sizes at least double, so few are kept)
+_ws_retired: Dict[tuple, list] = {}
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -68,13 +71,20 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     """Zero-initialised workspace for the current stream of ``device`` (grown on demand).
 
     The library keeps the workspace's synchronisation header zeroed between calls, so a
-    buffer is zero-filled only when first allocated."""
+    buffer is zero-filled only when first allocated. A buffer outgrown by a larger request is
+    not freed: calls prepared earlier (``prepare_*``) and graphs captured from them keep
+    pointing at it, so it stays referenced for the life of the process. Each replacement at
+    least doubles the size."""
     dev = torch.device(device)
     idx = dev.index if dev.index is not None else torch.cuda.current_device()
     key = (idx, torch.cuda.current_stream(dev).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, L.NORM_WS_HEADER_BYTES), dtype=torch.uint8, device=dev)
+        size = max(nbytes, L.NORM_WS_HEADER_BYTES)
+        if ws is not None:
+            size = max(size, 2 * ws.numel())
+            _ws_retired.setdefault(key, []).append(ws)
+        ws = torch.zeros(size, dtype=torch.uint8, device=dev)
         _ws_cache[key] = ws
     return ws
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.norm_abi_version() == 1
+    assert lib.norm_abi_version() == L.ABI_VERSION
 
 
 def test_enum_values_match_header():
@@ -215,7 +215,7 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
         mod.load()
 
 
-def test_colwise_rowmajor_layout_validation(monkeypatch):
+def test_colwise_rowmajor_layout_validation():
     mx = dict(out=L.NORM_FP8_E4M3, scaling=L.NORM_SCALING_MXFP8_1D32)
     rm = L.NORM_Q_COLWISE | L.NORM_Q_COLWISE_ROWMAJOR
     assert fwd_ws(64, 1024, layout=rm, **mx)[0] == L.NORM_OK
@@ -225,8 +225,9 @@ def test_colwise_rowmajor_layout_validation(monkeypatch):
     assert fwd_ws(64, 1024, layout=L.NORM_Q_ROWWISE | L.NORM_Q_COLWISE_ROWMAJOR, **mx)[0] == L.NORM_ERR_INVALID_ARG
     # served by the tile path only: rows longer than the row layouts, or the band kernel forced
     assert fwd_ws(16, 131072, layout=rm, **mx)[0] == L.NORM_ERR_UNSUPPORTED
-    monkeypatch.setenv("NORMFP8_COL_KERNEL", "0")
-    assert fwd_ws(64, 1024, layout=rm, **mx)[0] == L.NORM_ERR_UNSUPPORTED
+    with L.tuning(NORMFP8_COL_KERNEL=0):
+        assert fwd_ws(64, 1024, layout=rm, **mx)[0] == L.NORM_ERR_UNSUPPORTED
+    assert fwd_ws(64, 1024, layout=rm, **mx)[0] == L.NORM_OK
 
 
 def test_scales_padded_layout_validation():

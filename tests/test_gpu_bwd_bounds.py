@@ -1,0 +1,90 @@
+"""GPU regression: the backward's multi-team layouts at row counts that are not a multiple of
+their team count store nothing past dx, and still match the oracle.
+
+dx is carved from the front of a larger buffer whose tail holds a canary pattern; after the
+call the tail must be unchanged. Shapes are ones where the planner's defaults choose T = 2 or
+T = 4 teams per workgroup and rows % T != 0. Called through the C ABI with explicit pointers.
+
+[NVRTC-PR] "Migrate norms and softmax kernels to NVRTC", Flowchart (backward partial kernels and
+finalize); [BwdAdd] "Implementation: NVIDIA TransformerEngine Ops Fused Backward Add RMSNorm",
+I/O Contract (grad_input = RMSNorm backward + residual gradient, weight gradient).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import checks
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import rmsnorm_fp8_quantization_amd as nf  # noqa: E402
+from rmsnorm_fp8_quantization_amd import _lib as L, ops  # noqa: E402
+
+EPS = 1e-5
+CANARY_ROWS = 8
+CANARY = 0x5A
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _team_count(rows, hidden, norm_code, add):
+    shape = (ctypes.c_int64 * 5)()
+    L.call("norm_bwd_launch_shape", rows, hidden, L.NORM_BF16, L.NORM_F32, norm_code, add, 256, 0, 1, shape)
+    return int(shape[3])
+
+
+@pytest.mark.parametrize("rows,hidden", [(2049, 4096), (4097, 1024), (2049, 2048), (4099, 512)])
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm", "rmsnorm_add"])
+def test_multi_team_backward_stays_inside_dx(rows, hidden, kind):
+    norm = "layernorm" if kind == "layernorm" else "rmsnorm"
+    add = kind == "rmsnorm_add"
+    norm_code = L.NORM_LAYERNORM if norm == "layernorm" else L.NORM_RMSNORM
+    T = _team_count(rows, hidden, norm_code, int(add))
+    assert T > 1 and rows % T != 0, (T, rows)
+    print(f"bwd bounds: {kind} {rows}x{hidden} T={T}", flush=True)
+
+    case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=rows + hidden + int(add))
+    bits = workloads.to_numpy_bits
+    ref_f = oracle.forward_stored(bits(case["x"]), bits(case["gamma"]),
+                                  bits(case["beta"]) if norm == "layernorm" else None,
+                                  norm=norm, eps=EPS, in_dtype="bf16", w_dtype="f32")
+    ref = oracle.backward_stored(bits(case["dy"]), bits(case["x"]), ref_f["mu"], ref_f["rsigma"],
+                                 bits(case["gamma"]), norm=norm, in_dtype="bf16", w_dtype="f32",
+                                 residual_dy=bits(case["residual_dy"]) if add else None)
+    dev = torch.device("cuda")
+    dy, x, g = (case[k].to(dev) for k in ("dy", "x", "gamma"))
+    res = case["residual_dy"].to(dev) if add else None
+    mu = torch.tensor(ref_f["mu"], dtype=torch.float32, device=dev) if norm == "layernorm" else None
+    rs = torch.tensor(ref_f["rsigma"], dtype=torch.float32, device=dev)
+
+    # dx at the front of a buffer with CANARY_ROWS more rows of canary bytes behind it
+    buf = torch.full(((rows + CANARY_ROWS) * hidden * 2,), CANARY, dtype=torch.uint8, device=dev)
+    dx = buf[: rows * hidden * 2].view(torch.bfloat16).view(rows, hidden)
+    dg = torch.empty(hidden, dtype=torch.float32, device=dev)
+    db = torch.empty(hidden, dtype=torch.float32, device=dev) if norm == "layernorm" else None
+    nbytes = ops.bwd_workspace_size(rows, hidden, torch.bfloat16, torch.float32, norm, add)
+    ws = ops.workspace(nbytes, dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if add:
+        L.call("norm_bwd_add", stream, _p(dy), _p(x), _p(res), _p(rs), _p(g), _p(dx), _p(dg), _p(ws),
+               ws.numel(), rows, hidden, L.NORM_BF16, L.NORM_F32, 0, 0)
+    else:
+        L.call("norm_bwd", stream, _p(dy), _p(x), _p(mu), _p(rs), _p(g), _p(dx), _p(dg), _p(db), _p(ws),
+               ws.numel(), rows, hidden, L.NORM_BF16, L.NORM_F32, norm_code, 0, 0)
+    torch.cuda.synchronize()
+
+    tail = buf[rows * hidden * 2:].cpu().numpy()
+    assert np.all(tail == CANARY), f"{int((tail != CANARY).sum())} canary bytes behind dx overwritten"
+    checks.check_dx(workloads.to_numpy_bits(dx.cpu()), ref["dx"], "bf16")
+    checks.check_wgrad(dg.cpu().numpy(), ref["dgamma"])
+    if db is not None:
+        checks.check_wgrad(db.cpu().numpy(), ref["dbeta"], what="dbeta")

@@ -5,8 +5,6 @@ Shapes span several tiles and ragged tails; every forward layout (wave / workgro
 band split, columnwise band) is forced on small shapes through the planner's override knobs.
 Tolerances are those of tests/checks.py.
 """
-import contextlib
-import os
 
 import numpy as np
 import pytest
@@ -28,19 +26,9 @@ TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 EPS = 1e-5
 
 
-@contextlib.contextmanager
 def env(**kv):
-    old = {k: os.environ.get(k) for k in kv}
-    try:
-        for k, v in kv.items():
-            os.environ[k] = str(v)
-        yield
-    finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+    """Planner overrides for a block (norm_tuning_set through the binding)."""
+    return nf._lib.tuning(**kv)
 
 
 def bits(t):
