@@ -22,4 +22,4 @@ from .formats import (BF16, E4M3, E5M2, FORMATS, FP16, FP32, MX_EMAX, decode_sto
 from .norm import (LAYERNORM, RMSNORM, backward, backward_add, backward_stored,
                    delayed_epilogue, delayed_quantize, effective_gamma, forward,
                    forward_stored, mx_epilogue, mx_quantize_rows, normalized_values,
-                   plain_output, row_stats, scaled_f32)
+                   plain_output, row_stats)

@@ -19,9 +19,13 @@ each function below states the reading it implements:
     binary32; the normalised values are then evaluated in float64 from those
     binary32 statistics (the values a fused kernel stores and reuses).
   * zero-centred gamma: the effective weight is 1 + gamma; beta is unchanged.
-  * FP8 codes are decided in binary32, the precision of the fused epilogue: the
-    normalised value is rounded once to binary32, scaled in binary32, and that
-    binary32 value is rounded (nearest-even, saturating) to the FP8 grid.
+  * FP8 codes and MX exponents come from the unrounded float64 value: a delayed-
+    scaling code is one nearest-even, saturating rounding of v * scale (the scale
+    is a binary32 input); an MX block's exponent is taken from the float64 block
+    maximum, and its codes are one rounding of v * 2**-X.  (A binary32 kernel
+    reaches its codes through a chain of binary32 roundings; where that chain and
+    this single rounding disagree the value lies on a rounding boundary, which the
+    test-side checks verify element by element.)
   * Columnwise outputs are the same quantisation applied to the transposed
     matrix: layout [hidden, rows].
   * Backward: the exact gradient of sum(dy * y) with respect to x, gamma, beta,
@@ -31,8 +35,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import (FORMATS, FP32, decode_storage, encode_storage, e8m0_exponent,
-                      fp8_quantize, round_nearest_even, to_f32)
+from .formats import FORMATS, decode_storage, encode_storage, e8m0_exponent, fp8_quantize, to_f32
 
 LAYERNORM = "layernorm"
 RMSNORM = "rmsnorm"
@@ -106,15 +109,10 @@ def plain_output(v, out_dtype: str):
 # and updated amax out)
 # ----------------------------------------------------------------------------------------
 
-def scaled_f32(v, factor):
-    """binary32 normalised value times a binary32 factor, rounded to binary32."""
-    y32 = to_f32(v)
-    return to_f32(y32 * np.float64(np.float32(factor)))
-
-
 def delayed_quantize(v, scale: float, fp8: str):
-    """Per-tensor delayed scaling of a value matrix: codes = fp8(y32 * scale)."""
-    return fp8_quantize(scaled_f32(v, scale), FORMATS[fp8])
+    """Per-tensor delayed scaling of a value matrix: codes = fp8(v * scale), one saturating
+    nearest-even rounding of the float64 product of v and the binary32 scale."""
+    return fp8_quantize(np.asarray(v, dtype=np.float64) * np.float64(np.float32(scale)), FORMATS[fp8])
 
 
 def delayed_epilogue(v, scale: float, amax_in: float, fp8: str, colwise: bool):
@@ -141,16 +139,15 @@ def mx_quantize_rows(v, fp8: str, block: int = 32, rule: str = "floor"):
     v = np.asarray(v, dtype=np.float64)
     r, c = v.shape
     nb = -(-c // block)
-    y32 = to_f32(v)
     codes = np.zeros((r, c), dtype=np.uint8)
     scales = np.zeros((r, nb), dtype=np.uint8)
     for b in range(nb):
-        blk = y32[:, b * block:(b + 1) * block]
+        blk = v[:, b * block:(b + 1) * block]
         a = np.max(np.abs(blk), axis=1) if blk.shape[1] else np.zeros(r)
         x = e8m0_exponent(a, fp8, rule)
         scales[:, b] = (x + 127).astype(np.uint8)
         scaled = blk * np.ldexp(1.0, (-x)[:, None])       # exact power-of-two scaling
-        codes[:, b * block:(b + 1) * block] = fp8_quantize(round_nearest_even(scaled, FP32), fmt)
+        codes[:, b * block:(b + 1) * block] = fp8_quantize(scaled, fmt)
     return codes, scales
 
 

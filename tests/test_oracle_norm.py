@@ -160,8 +160,9 @@ def test_delayed_scale_inv_known_values():
 
 
 def test_delayed_codes_bruteforce_small():
-    """Per-element scalar recomputation: y32 = f32(v), u = f32(y32 * s), code = nearest
-    finite E5M2 value by exhaustive search over the 256 codes (ties to the even code)."""
+    """Per-element scalar recomputation: u = v * s (one product of the unrounded value and the
+    binary32 scale), code = nearest finite E5M2 value by exhaustive search over the 256 codes
+    (ties to the even code)."""
     v = _rand((3, 40), 15) * 3.0
     s = 1234.5
     codes = N.delayed_quantize(v, s, "e5m2")
@@ -169,7 +170,7 @@ def test_delayed_codes_bruteforce_small():
     fin = [c for c in range(256) if math.isfinite(table[c])]
     for r in range(3):
         for c in range(40):
-            u = float(np.float32(np.float32(v[r, c]) * np.float32(s)))
+            u = float(v[r, c]) * float(np.float32(s))
             u = max(-57344.0, min(57344.0, u))
             best = min(fin, key=lambda k: (abs(table[k] - u), k % 2, k))
             assert F.fp8_decode(np.array([codes[r, c]]), F.E5M2)[0] == table[best]
@@ -183,7 +184,7 @@ def test_mx_rowwise_bruteforce_small():
     fin = [c for c in range(256) if math.isfinite(table[c])]
     for r in range(2):
         for b in range(3):
-            blk = [float(np.float32(t)) for t in v[r, 32 * b:32 * b + 32]]
+            blk = [float(t) for t in v[r, 32 * b:32 * b + 32]]
             a = max(abs(t) for t in blk)
             x = math.floor(math.log2(a)) - 8
             assert scales[r, b] == x + 127
@@ -218,7 +219,7 @@ def test_mx_colwise_rowmajor_bruteforce_small():
     fin = [c for c in range(256) if math.isfinite(table[c])]
     for j in range(3):
         for b in range(3):
-            blk = [float(np.float32(t)) for t in v[32 * b:32 * b + 32, j]]
+            blk = [float(t) for t in v[32 * b:32 * b + 32, j]]
             a = max(abs(t) for t in blk)
             x = math.floor(math.log2(a)) - 8
             assert scales[b, j] == x + 127
@@ -266,6 +267,73 @@ def test_backward_matches_central_finite_differences(norm, rows, h):
         assert np.allclose(got["dbeta"], db, rtol=1e-5, atol=1e-6)
     else:
         assert got["dbeta"] is None
+
+
+def _fd(fn, arr):
+    out = np.zeros_like(arr)
+    it = np.nditer(arr, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        hstep = 1e-6 * max(1.0, abs(arr[i]))
+        a1 = arr.copy(); a1[i] += hstep
+        a2 = arr.copy(); a2[i] -= hstep
+        out[i] = (fn(a1) - fn(a2)) / (2 * hstep)
+    return out
+
+
+@pytest.mark.parametrize("norm", [N.LAYERNORM, N.RMSNORM])
+@pytest.mark.parametrize("rows,h", [(1, 1), (2, 3), (3, 8), (1, 33)])
+def test_zero_centered_backward_matches_finite_differences(norm, rows, h):
+    """backward_stored with zero_centered_gamma against central differences of
+    L = sum(dy * y) where y is the zero-centred forward (weight 1 + gamma) and gamma is the raw
+    parameter ([XLA-Norm] Signature / I/O Contract: zero_centered_gamma is an input of the
+    forward and of the backward). A backward that dropped the + 1 would use the weight gamma
+    (about 0.05 here) instead of about 1, and fail by a factor of ~20."""
+    eps = 1e-3
+    f32 = lambda a: np.asarray(a, np.float32)  # stored float32 tensors, exact in float64
+    x = f32(_rand((rows, h), 500 + h, 0.5, 2.0)).astype(np.float64)
+    gamma = f32(_rand(h, 600 + h, 0.0, 0.05)).astype(np.float64)
+    beta = f32(_rand(h, 700 + h, 0.0, 0.3)).astype(np.float64) if norm == N.LAYERNORM else None
+    dy = f32(_rand((rows, h), 800 + h)).astype(np.float64)
+
+    def loss(xa, ga, ba):
+        v = N.forward(xa, ga, ba, norm, eps, zero_centered_gamma=True, round_stats=False)["v"]
+        return float((dy * v).sum())
+
+    mu, rs = N.row_stats(x, norm, eps, round_to_f32=True)
+    got = N.backward_stored(f32(dy), f32(x), mu, rs, f32(gamma), norm=norm, in_dtype="f32", w_dtype="f32",
+                            zero_centered_gamma=True)
+    dx = _fd(lambda a: loss(a, gamma, beta), x)
+    dg = _fd(lambda a: loss(x, a, beta), gamma)
+    # binary32 statistics in the backward: ~1e-7 relative against the exact-statistics differences
+    assert np.allclose(got["dx"], dx, rtol=1e-5, atol=1e-5 * max(1.0, np.abs(dx).max()))
+    assert np.allclose(got["dgamma"], dg, rtol=1e-5, atol=1e-5 * max(1.0, np.abs(dg).max()))
+    if norm == N.LAYERNORM:
+        db = _fd(lambda a: loss(x, gamma, a), beta)
+        assert np.allclose(got["dbeta"], db, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("norm", [N.LAYERNORM, N.RMSNORM])
+def test_zero_centered_backward_is_backward_at_one_plus_gamma(norm):
+    """backward(gamma, zero-centred) is bitwise backward(1 + gamma, plain) for weights whose
+    1 + gamma is exact in float32 (multiples of 2^-10 below 1)."""
+    h = 96
+    x = np.asarray(_rand((5, h), 61, 0.5, 2.0), np.float32)
+    dy = np.asarray(_rand((5, h), 62), np.float32)
+    gamma = np.asarray(np.round(_rand(h, 63, 0.0, 0.05) * 1024) / 1024, np.float32)
+    gamma1 = gamma + np.float32(1.0)
+    assert np.array_equal(gamma1.astype(np.float64), gamma.astype(np.float64) + 1.0)
+    mu, rs = N.row_stats(x.astype(np.float64), norm, 1e-5)
+    kw = dict(norm=norm, in_dtype="f32", w_dtype="f32")
+    zc = N.backward_stored(dy, x, mu, rs, gamma, zero_centered_gamma=True, **kw)
+    plain = N.backward_stored(dy, x, mu, rs, gamma1, zero_centered_gamma=False, **kw)
+    raw = N.backward_stored(dy, x, mu, rs, gamma, zero_centered_gamma=False, **kw)
+    assert np.array_equal(zc["dx"], plain["dx"]) and np.array_equal(zc["dgamma"], plain["dgamma"])
+    assert not np.allclose(zc["dx"], raw["dx"])       # the flag is not a no-op
+    # dgamma does not depend on the weight (d(1 + gamma)/dgamma = 1): sum of dy * xhat
+    assert np.array_equal(zc["dgamma"], raw["dgamma"])
+    if norm == N.LAYERNORM:
+        assert np.array_equal(zc["dbeta"], plain["dbeta"])
 
 
 @pytest.mark.parametrize("norm", [N.LAYERNORM, N.RMSNORM])
