@@ -282,17 +282,24 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     pl->tile_rows = kBandShapes[bc].rows();
     pl->S = (int)cdiv(hidden, kBandShapes[bc].cols());
     pl->bands = cdiv(rows, pl->tile_rows);
-    if (pl->S > kMaxSlices)
-      return fail(NORM_ERR_UNSUPPORTED, "hidden %lld needs %d workgroups per band; this build allows %d",
-                  (long long)hidden, pl->S, kMaxSlices);
+    if (pl->S > kMaxSlices) {
+      // more slices than a band can merge (columnwise output of rows beyond 64 K elements):
+      // the general kernels, a row pass and a column pass
+      if (col_rowmajor)
+        return fail(NORM_ERR_UNSUPPORTED, "the row-major columnwise layout needs hidden <= 65536");
+      pl->gen = true;
+      pl->band = false;
+      pl->S = 1;
+    }
   }
 
   // workspace: header when the launch coordinates workgroups, then band partials
   const bool header = pl->mode == MODE_DELAYED || (pl->band && pl->S > 1);
+  if (pl->gen) pl->cfg = 0;
   size_t ws = header ? (size_t)kWsHeaderBytes : 0;
   if (pl->band && pl->S > 1) {
     pl->partial_off = ws;
-    const int nv = norm_type == NORM_LAYERNORM ? 2 : 1;
+    const int nv = norm_type == NORM_LAYERNORM ? 3 : 1;  // (mean, M2, shift) or the sum of squares
     ws += round_up((size_t)pl->bands * pl->S * pl->tile_rows * nv * sizeof(uint64_t), 256);
   }
   // row statistics of a columnwise request (two-pass paths; sized for every columnwise request,

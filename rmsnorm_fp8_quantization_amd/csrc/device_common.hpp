@@ -252,8 +252,8 @@ __device__ __forceinline__ float exp2_neg(int x) {
 
 // ------------------------------------------------------------------------------------------
 // cross-lane reductions (wave64). Quad and row steps use DPP; the 16- and 32-lane steps use
-// ds_swizzle / ds_bpermute. Every lane ends with the same value: each step combines a lane
-// with a partner using a commutative operation.
+// lane swaps. Every lane ends with the same value: each step combines a lane with a partner
+// using a commutative operation.
 // ------------------------------------------------------------------------------------------
 
 #define NF8_DPP(ctrl) \
@@ -263,12 +263,21 @@ __device__ __forceinline__ float xor1(float v) { return NF8_DPP(0xB1); }   // qu
 __device__ __forceinline__ float xor2(float v) { return NF8_DPP(0x4E); }   // quad_perm [2,3,0,1]
 __device__ __forceinline__ float hmirror(float v) { return NF8_DPP(0x141); } // row_half_mirror
 __device__ __forceinline__ float mirror(float v) { return NF8_DPP(0x140); }  // row_mirror
+// The 16- and 32-lane steps use gfx950's lane-swap instructions (VALU, no LDS round trip):
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with the even rows of
+// its second, v_permlane32_swap the upper half of the first with the lower half of the second.
+// With both operands v, result[0] holds the even rows (lower half) and result[1] the odd rows
+// (upper half) in both positions, so lane l's partner l ^ 16 (l ^ 32) is result[1] where l is in
+// an even row (the lower half) and result[0] otherwise. Every lane of the wave must be active.
 __device__ __forceinline__ float xor16(float v) {
-  return __uint_as_float((uint32_t)__builtin_amdgcn_ds_swizzle((int)__float_as_uint(v), (16 << 10) | 0x1f));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __uint_as_float((lane & 16) == 0 ? r[1] : r[0]);
 }
 __device__ __forceinline__ float xor32(float v) {
-  int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  return __uint_as_float((uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, (int)__float_as_uint(v)));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __uint_as_float((lane & 32) == 0 ? r[1] : r[0]);
 }
 #undef NF8_DPP
 
@@ -319,6 +328,25 @@ __device__ __forceinline__ Stats chan_merge(const Stats &a, const Stats &b) {
   r.mean = a_only ? a.mean : (b_only ? b.mean : r.mean);
   r.m2 = a_only ? a.m2 : (b_only ? b.m2 : r.m2);
   return r;
+}
+
+// the value of `v` in the wave's first active lane (lane 0 where every lane is active)
+__device__ __forceinline__ float first_lane(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// LayerNorm partial statistics taken relative to a shift K (the first element of the row
+// piece a wave holds): sums of x - K instead of x, so that a row whose values share a large
+// common part (x = 1000 + 0.01 * noise) keeps its deviations; x - K is exact for values
+// within a factor of two of K. `s.mean` is relative to `k`.
+struct ShiftedStats {
+  Stats s;
+  float k;
+};
+// `o` moved into the frame of shift `k`: its mean relative to k is (o.k - k) + o.s.mean, where
+// o.k - k is exact when the shifts are close and otherwise small against the deviations
+__device__ __forceinline__ Stats in_frame(const ShiftedStats &o, float k) {
+  return Stats{o.s.n, (o.k - k) + o.s.mean, o.s.m2};
 }
 
 __device__ __forceinline__ int lane_id() {

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
   const int64_t N = p.rows;
   const int fmt = p.out_dtype;
 
-  constexpr int NV = NORM == NT_LAYERNORM ? 2 : 1;  // tagged words per row partial
+  constexpr int NV = NORM == NT_LAYERNORM ? 3 : 1;  // tagged words per row partial (mean, M2, shift)
   __shared__ int64_t s_next;
   __shared__ uint32_t s_last;
   __shared__ uint32_t s_epoch;
@@ -173,12 +173,28 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
         else zero_strip<IN>(xs[j][k]);
       }
 
-    // ---- per-row partial statistics of this slice (wave-merged)
+    // ---- per-row partial statistics of this slice (wave-merged). LayerNorm: taken relative
+    // to a shift K near the mean -- the slice's plain mean estimate of the row -- so that a row
+    // with a large common part keeps its deviations
     Stats st[RW];
+    float shift[RW];
+    const float inv_ns = 1.0f / (float)(H - cbase < CW ? H - cbase : CW);  // this slice's columns
 #pragma unroll
     for (int j = 0; j < RW; ++j) {
       const bool rv = rbase + j < N;
+      shift[j] = 0.0f;
       if constexpr (NORM == NT_LAYERNORM) {
+        {
+          float sa = 0.0f;
+#pragma unroll
+          for (int k = 0; k < KC; ++k) {
+            float xv[8];
+            strip_to_f32<IN>(xs[j][k], xv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sa += xv[i];  // (strips outside the tensor are zero)
+          }
+          shift[j] = first_lane(wave_sum(sa) * inv_ns);  // rounded once (no fma fusion into x - K)
+        }
         float sm = 0.0f, n = 0.0f;
 #pragma unroll
         for (int k = 0; k < KC; ++k) {
@@ -186,7 +202,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
           strip_to_f32<IN>(xs[j][k], xv);
           if (rv && cv[k]) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) sm += xv[i];
+            for (int i = 0; i < 8; ++i) sm += xv[i] - shift[j];
             n += 8.0f;
           }
         }
@@ -199,7 +215,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
           if (rv && cv[k]) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              const float d = xv[i] - m;
+              const float d = (xv[i] - shift[j]) - m;
               q = fmaf(d, d, q);
             }
           }
@@ -230,6 +246,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
           if constexpr (NORM == NT_LAYERNORM) {
             st_dev64(part + (wave * RW + j) * NV, tagged(st[j].mean, tag));
             st_dev64(part + (wave * RW + j) * NV + 1, tagged(st[j].m2, tag));
+            st_dev64(part + (wave * RW + j) * NV + 2, tagged(shift[j], tag));
           } else {
             st_dev64(part + (wave * RW + j), tagged(st[j].m2, tag));
           }
@@ -245,12 +262,15 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
 #pragma unroll
       for (int j = 0; j < RW; ++j) {
         Stats acc{0.0f, 0.0f, 0.0f};
+        float k0 = 0.0f;
         if (lane == j) {
+          if constexpr (NORM == NT_LAYERNORM) k0 = xpart[wave][j][0][2];  // slice 0's frame
           for (int sl = 0; sl < S; ++sl) {
             if constexpr (NORM == NT_LAYERNORM) {
               const int64_t left = H - (int64_t)sl * CW;
               const float n = (float)(left < CW ? left : CW);
-              acc = chan_merge(acc, Stats{n, xpart[wave][j][sl][0], xpart[wave][j][sl][1]});
+              const ShiftedStats o{Stats{n, xpart[wave][j][sl][0], xpart[wave][j][sl][1]}, xpart[wave][j][sl][2]};
+              acc = chan_merge(acc, in_frame(o, k0));
             } else {
               acc.m2 += xpart[wave][j][sl][0];
             }
@@ -258,6 +278,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
         }
         st[j].mean = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc.mean), j));
         st[j].m2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc.m2), j));
+        shift[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, k0), j));
       }
     }
     // The next tile's ticket is taken only now, once this workgroup waits for nothing more in
@@ -268,7 +289,7 @@ __global__ __launch_bounds__(256) void fwd_band_kernel(FwdBandParams bp) {
     float mu[RW], rs[RW];
 #pragma unroll
     for (int j = 0; j < RW; ++j) {
-      mu[j] = NORM == NT_LAYERNORM ? st[j].mean : 0.0f;
+      mu[j] = NORM == NT_LAYERNORM ? shift[j] + st[j].mean : 0.0f;
       rs[j] = 1.0f / sqrtf(st[j].m2 * inv_h + p.eps);
       const int64_t row = rbase + j;
       if (slice == 0 && lane == j && row < N) {

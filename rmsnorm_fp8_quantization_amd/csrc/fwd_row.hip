@@ -56,7 +56,6 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
     cv[k] = 8 * (int64_t)(tl + TEAM * k) < H;
     n_in += cv[k] ? 8.0f : 0.0f;
   }
-  const float n_out = 8.0f * KC - n_in;  // zeroed strip elements
 
   // ---- weights
   __shared__ float wlds[WL == 1 && MODE != MODE_STATS ? NW * COVER : 1];  // (statistics: no weights)
@@ -159,8 +158,10 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
   }
   float amax_local = 0.0f;
 
-  __shared__ Stats red[2][T][P];
+  __shared__ ShiftedStats red[2][T][P];
   const float inv_h = 1.0f / (float)H;
+  // reciprocal of the number of row elements this wave holds (LayerNorm's shift estimate)
+  const float inv_nw = P == 1 ? inv_h : 1.0f / fmaxf(wave_sum(n_in), 1.0f);
   const int64_t stride = (int64_t)gridDim.x * T;
 
   // Loads are unconditional (rows past the end read row 0, strips past the end of the row read
@@ -199,21 +200,42 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
       for (int k = 0; k < WLA && k < KC; ++k) weights_raw(k, wq_g[k], wq_b[k]);
     }
 
-    // ---- lane-local statistics over its valid strips
+    // ---- lane-local statistics over its valid strips. LayerNorm takes every deviation from a
+    // shift K near the mean -- the wave's plain mean estimate (sum of its elements over their
+    // count) -- so that a row whose values share a large common part keeps its deviations, and
+    // the mean comes out as K + (mean - K), rounded once; strips past the end add nothing.
     Stats st{0.0f, 0.0f, 0.0f};
-    if constexpr (NORM == NT_LAYERNORM && P == 1) {
-      // one wave holds the row: the exact two-pass form, mean first, then the sum of squared
-      // deviations from it (strips past the end are zero; each adds mean^2 per element to
-      // the second sum, taken off again)
+    float shift = 0.0f;
+    if constexpr (NORM == NT_LAYERNORM) {
+      {
+        float sa = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          float xv[8];
+          strip_to_f32<IN>(cur[k], xv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sa += xv[i];  // (strips past the end are zero)
+        }
+        // (through readfirstlane: the shift is rounded once and every use sees that value; a
+        // product left in a register would be fused into each x - K as an fma, putting the
+        // deviations in a frame of the unrounded product)
+        shift = first_lane(wave_sum(sa) * inv_nw);
+      }
+      if constexpr (RECONV) {
+#pragma unroll
+        for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
+      }
       float sm = 0.0f;
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
         float xv[8];
         strip_to_f32<IN>(cur[k], xv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sm += xv[i];
+        for (int i = 0; i < 8; ++i) sm += cv[k] ? xv[i] - shift : 0.0f;
       }
-      const float m = wave_sum(sm) * inv_h;
+      // one wave per row: the exact two-pass form (the row's shifted mean, then the squared
+      // deviations from it); several waves: per-lane (n, mean, M2) merged in the Chan form
+      const float m = P == 1 ? wave_sum(sm) * inv_h : (n_in > 0.0f ? sm * __builtin_amdgcn_rcpf(n_in) : 0.0f);
       if constexpr (RECONV) {
 #pragma unroll
         for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
@@ -225,41 +247,12 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
         strip_to_f32<IN>(cur[k], xv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float d = xv[i] - m;
+          const float d = cv[k] ? (xv[i] - shift) - m : 0.0f;
           q = fmaf(d, d, q);
         }
       }
-      q = fmaf(-n_out * m, m, q);
-      st = Stats{(float)H, m, wave_sum(q)};
-    } else if constexpr (NORM == NT_LAYERNORM) {
-      // several waves per row: per-lane (n, mean, M2), merged in the Chan form
-      float sm = 0.0f;
-#pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        float xv[8];
-        strip_to_f32<IN>(cur[k], xv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sm += xv[i];
-      }
-      const float n = n_in;
-      const float m = n > 0.0f ? sm * __builtin_amdgcn_rcpf(n) : 0.0f;
-      if constexpr (RECONV) {
-#pragma unroll
-        for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
-      }
-      float q = 0.0f;
-#pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        float xv[8];
-        strip_to_f32<IN>(cur[k], xv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float d = xv[i] - m;
-          q = fmaf(d, d, q);
-        }
-      }
-      q = fmaf(-n_out * m, m, q);
-      st = wave_merge(Stats{n, m, q});
+      if constexpr (P == 1) st = Stats{(float)H, m, wave_sum(q)};
+      else st = wave_merge(Stats{n_in, m, q});
     } else {
       float q = 0.0f;
 #pragma unroll
@@ -272,20 +265,22 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
       st.m2 = wave_sum(q);
     }
 
-    // ---- merge the team's waves in a fixed order
+    // ---- merge the team's waves in a fixed order (LayerNorm: each wave's partial moved into
+    // wave 0's frame)
     if constexpr (P > 1) {
-      if (lane == 0) red[iter & 1][team][wt] = st;
+      if (lane == 0) red[iter & 1][team][wt] = ShiftedStats{st, shift};
       __syncthreads();
-      st = red[iter & 1][team][0];
+      st = red[iter & 1][team][0].s;
+      shift = red[iter & 1][team][0].k;
 #pragma unroll
       for (int w = 1; w < P; ++w) {
-        const Stats o = red[iter & 1][team][w];
-        if constexpr (NORM == NT_LAYERNORM) st = chan_merge(st, o);
-        else st.m2 += o.m2;
+        const ShiftedStats o = red[iter & 1][team][w];
+        if constexpr (NORM == NT_LAYERNORM) st = chan_merge(st, in_frame(o, shift));
+        else st.m2 += o.s.m2;
       }
     }
 
-    const float mu = NORM == NT_LAYERNORM ? st.mean : 0.0f;
+    const float mu = NORM == NT_LAYERNORM ? shift + st.mean : 0.0f;
     const float rs = __builtin_amdgcn_rsqf(st.m2 * inv_h + p.eps);
     if constexpr (RECONV) {
 #pragma unroll

@@ -64,6 +64,19 @@ __device__ __forceinline__ uint8_t fp8_code1(float u, int fmt) {
   return (uint8_t)(w & 0xff);
 }
 
+// Compensated (Neumaier) running sum: a lane of the general kernels adds up to H / 64 terms of
+// a row in sequence, and the compensation keeps the total within a few ulps however long the
+// row is (a plain float32 running sum drifts by about sqrt(n) ulps).
+struct CSum {
+  float s = 0.0f, c = 0.0f;
+  __device__ __forceinline__ void add(float v) {
+    const float t = s + v;
+    c += fabsf(s) >= fabsf(v) ? (s - t) + v : (v - t) + s;
+    s = t;
+  }
+  __device__ __forceinline__ float value() const { return s + c; }
+};
+
 // max over the 32 lanes of a half-wave (lanes l and l ^ 1, ^ 2, mirrored 8 / 16, ^ 16)
 __device__ __forceinline__ float halfwave_max(float v) {
   v = fmaxf(v, xor1(v));
@@ -101,27 +114,37 @@ __global__ __launch_bounds__(256) void fwd_gen_row_kernel(FwdRowParams p) {
     float mean = 0.0f;
     float m2;
     if constexpr (NORM == NT_LAYERNORM) {
-      float s = 0.0f;
+      // deviations from a shift K near the mean (a plain first estimate of it), so that a large
+      // common part of the row does not swamp them (x - K is exact for values within a factor
+      // of two of K); the mean is then K + (mean - K), rounded once
+      CSum s0;
       for (int64_t j = 0; j < nj; ++j) {
         const int64_t i = j * 64 + lane;
-        s += i < H ? ld1<IN>(xr, i) : 0.0f;
+        s0.add(i < H ? ld1<IN>(xr, i) : 0.0f);
       }
-      mean = wave_sum(s) * inv_h;
-      float q = 0.0f;
+      const float shift = first_lane(wave_sum(s0.value()) * inv_h);  // rounded once (no fma fusion into x - K)
+      CSum s;
       for (int64_t j = 0; j < nj; ++j) {
         const int64_t i = j * 64 + lane;
-        const float d = i < H ? ld1<IN>(xr, i) - mean : 0.0f;
-        q = fmaf(d, d, q);
+        s.add(i < H ? ld1<IN>(xr, i) - shift : 0.0f);
       }
-      m2 = wave_sum(q);
+      const float ms = wave_sum(s.value()) * inv_h;
+      CSum q;
+      for (int64_t j = 0; j < nj; ++j) {
+        const int64_t i = j * 64 + lane;
+        const float d = i < H ? (ld1<IN>(xr, i) - shift) - ms : 0.0f;
+        q.add(d * d);
+      }
+      mean = shift + ms;
+      m2 = wave_sum(q.value());
     } else {
-      float q = 0.0f;
+      CSum q;
       for (int64_t j = 0; j < nj; ++j) {
         const int64_t i = j * 64 + lane;
         const float v = i < H ? ld1<IN>(xr, i) : 0.0f;
-        q = fmaf(v, v, q);
+        q.add(v * v);
       }
-      m2 = wave_sum(q);
+      m2 = wave_sum(q.value());
     }
     const float rs = __builtin_amdgcn_rsqf(m2 * inv_h + p.eps);
     if (lane == 0) {
