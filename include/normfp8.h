@@ -196,6 +196,23 @@ int norm_bwd_add(void *stream, const void *dy, const void *x, const void *residu
                  size_t workspace_bytes, int64_t rows, int64_t hidden, int in_dtype, int w_dtype,
                  int zero_centered_gamma, int cu_margin);
 
+/*
+ * norm_bwd_noalloc -- norm_bwd without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Arguments, results and errors are those of norm_bwd; the scratch memory the
+ * backward's kernels need (the per-workgroup weight-gradient partials) is a static device array
+ * of NORM_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until the process ends.
+ * The call allocates nothing. Shapes whose workspace query exceeds the array (LayerNorm rows of
+ * more than about 16 K elements, RMSNorm of more than about 32 K) return NORM_ERR_UNSUPPORTED.
+ * All calls on one GPU share its array: two calls that may overlap on one GPU (different
+ * streams, or different threads without ordering) race and corrupt each other's gradients;
+ * serialise them, or use norm_bwd with one workspace per stream.
+ */
+#define NORM_NOALLOC_SCRATCH_BYTES (32u << 20)
+int norm_bwd_noalloc(void *stream, const void *dy, const void *x, const float *mu, const float *rsigma,
+                     const void *gamma, void *dx, void *dgamma, void *dbeta, int64_t rows, int64_t hidden,
+                     int in_dtype, int w_dtype, int norm_type, int zero_centered_gamma, int cu_margin);
+
 /* Zero the synchronisation header of a new workspace (enqueues one small kernel on stream). */
 int norm_workspace_init(void *stream, void *workspace, size_t workspace_bytes);
 

@@ -25,7 +25,7 @@ NORM_Q_SCALES_PADDED = 8
 NORM_WS_HEADER_BYTES = 16384
 
 EXPORTS = ("norm_fwd_workspace_size", "norm_bwd_workspace_size", "norm_fwd", "norm_bwd",
-           "norm_bwd_add", "norm_workspace_init", "norm_workspace_check", "norm_bwd_launch_shape",
+           "norm_bwd_add", "norm_bwd_noalloc", "norm_workspace_init", "norm_workspace_check", "norm_bwd_launch_shape",
            "norm_tuning_set", "norm_last_error", "norm_abi_version")
 ABI_VERSION = 2
 KNOB_UNSET = -2 ** 31  # INT_MIN: a tuning override that is not set
@@ -43,6 +43,7 @@ _SIGS = {
                  _I64, _I64, _I, _I, _I, _I, _I, _I, _I, _F, _I],
     "norm_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I, _I, _I, _I, _I],
     "norm_bwd_add": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I64, _I64, _I, _I, _I, _I],
+    "norm_bwd_noalloc": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I, _I],
     "norm_workspace_init": [_P, _P, _SZ],
     "norm_workspace_check": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
     "norm_bwd_launch_shape": [_I64, _I64, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I64)],

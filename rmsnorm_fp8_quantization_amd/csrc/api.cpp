@@ -401,6 +401,10 @@ int check_ws(void *ws, size_t have, size_t need) {
 
 }  // namespace
 
+namespace nf8 {
+int set_last_error(int code, const char *msg) { return fail(code, "%s", msg); }
+}  // namespace nf8
+
 // ================================================================ C ABI
 extern "C" {
 

@@ -93,4 +93,7 @@ const void *bwd_kernel_ptr(int norm, int in_dtype, bool add, int cfg);
 const void *bwd_finalize_kernel_ptr();
 const void *ws_init_kernel_ptr();
 
+// host side: record `msg` as the calling thread's norm_last_error() and return `code`
+int set_last_error(int code, const char *msg);
+
 }  // namespace nf8
