@@ -225,34 +225,42 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
 #pragma unroll
         for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
       }
-      float sm = 0.0f;
+      // one pass over the deviations d = x - K of the valid elements: their sum and sum of
+      // squares. With K near the mean the lane's (and the row's) mean deviation is small
+      // against the spread, so M2 = sum d^2 - (sum d)^2 / n loses nothing to cancellation.
+      // Strip k is inside the row for every lane of the team when 8 * TEAM * (k + 1) <= H (a
+      // uniform test); only other strips need the per-lane mask.
+      float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
         float xv[8];
         strip_to_f32<IN>(cur[k], xv);
+        if (8 * (int64_t)TEAM * (k + 1) <= H) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sm += cv[k] ? xv[i] - shift : 0.0f;
-      }
-      // one wave per row: the exact two-pass form (the row's shifted mean, then the squared
-      // deviations from it); several waves: per-lane (n, mean, M2) merged in the Chan form
-      const float m = P == 1 ? wave_sum(sm) * inv_h : (n_in > 0.0f ? sm * __builtin_amdgcn_rcpf(n_in) : 0.0f);
-      if constexpr (RECONV) {
+          for (int i = 0; i < 8; ++i) {
+            const float d = xv[i] - shift;
+            s1 += d;
+            s2 = fmaf(d, d, s2);
+          }
+        } else {
 #pragma unroll
-        for (int k = 0; k < KC; ++k) opaque<IN>(cur[k]);
-      }
-      float q = 0.0f;
-#pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        float xv[8];
-        strip_to_f32<IN>(cur[k], xv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float d = cv[k] ? (xv[i] - shift) - m : 0.0f;
-          q = fmaf(d, d, q);
+          for (int i = 0; i < 8; ++i) {
+            const float d = cv[k] ? xv[i] - shift : 0.0f;
+            s1 += d;
+            s2 = fmaf(d, d, s2);
+          }
         }
       }
-      if constexpr (P == 1) st = Stats{(float)H, m, wave_sum(q)};
-      else st = wave_merge(Stats{n_in, m, q});
+      if constexpr (P == 1) {
+        // one wave holds the row: its mean deviation and M2 directly
+        const float t1 = wave_sum(s1), t2 = wave_sum(s2);
+        const float m = t1 * inv_h;
+        st = Stats{(float)H, m, fmaxf(fmaf(-t1, m, t2), 0.0f)};
+      } else {
+        // several waves: per-lane (n, mean, M2), merged in the Chan form
+        const float m = n_in > 0.0f ? s1 * __builtin_amdgcn_rcpf(n_in) : 0.0f;
+        st = wave_merge(Stats{n_in, m, fmaxf(fmaf(-s1, m, s2), 0.0f)});
+      }
     } else {
       float q = 0.0f;
 #pragma unroll
