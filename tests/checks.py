@@ -73,7 +73,7 @@ def check_stats(mu_g, rs_g, mu_ref, rs_ref, rows_sigma=None):
         assert np.all(e2 <= TOL["mu"]), f"mu max rel err {e2.max():.3e}"
 
 
-def check_hp(y_g: np.ndarray, v: np.ndarray, dtype: str, what="y", terms=None):
+def check_hp(y_g: np.ndarray, v: np.ndarray, dtype: str, what="y", terms=None, aggregate=False):
     """High-precision output (f32 / f16 / bf16 storage) against unrounded v.
 
     16-bit outputs: at most 1 ulp from the nearest-even rounding of v. Where y is the small
@@ -88,7 +88,7 @@ def check_hp(y_g: np.ndarray, v: np.ndarray, dtype: str, what="y", terms=None):
         den = np.maximum(np.abs(v), rms)
         err = np.abs(g - v) / np.where(den > 0, den, 1.0)
         assert np.all(err <= TOL["f32"]), f"{what}: max rel err {err.max():.3e}"
-        return Report(max_err=float(err.max()))
+        return Report(max_err=float(err.max()), n=int(g.size), cancellation=0, off_by_one=0)
     ref = oracle.encode_storage(v, dtype)
     raw = np.asarray(y_g).view(np.uint16)
     d = np.abs(_ordered(raw, 16) - _ordered(np.asarray(ref).view(np.uint16), 16))
@@ -101,7 +101,7 @@ def check_hp(y_g: np.ndarray, v: np.ndarray, dtype: str, what="y", terms=None):
         n_cancel = int((far & ok).sum())
         far = far & ~ok
     assert not far.any(), f"{what}: {int(far.sum())} elements more than 1 ulp off"
-    assert n_cancel <= allowance_budget(d.size), \
+    assert aggregate or n_cancel <= allowance_budget(d.size), \
         f"{what}: {n_cancel} of {d.size} elements pass only through the cancellation allowance"
     return Report(off_by_one=int((d == 1).sum()), cancellation=n_cancel, n=int(d.size))
 
@@ -182,7 +182,7 @@ def check_delayed(out, v, scale, amax_in, fp8, rowwise=True, colwise=False, term
     return rep
 
 
-def check_mx_rows(codes_g, scales_g, v, fp8, what="mx", terms=None, rule="floor"):
+def check_mx_rows(codes_g, scales_g, v, fp8, what="mx", terms=None, rule="floor", aggregate=False):
     """MXFP8 blocks along the last axis of v (float64 [r, c]) against GPU codes / scale bytes
     (terms: LayerNorm term magnitudes laid out like v, see the module docstring; rule: the
     E8M0 exponent rule, whose decision boundaries are the powers of two for "floor" and
@@ -224,13 +224,42 @@ def check_mx_rows(codes_g, scales_g, v, fp8, what="mx", terms=None, rule="floor"
         rb = check_fp8(codes_g[:, sl], ref_codes, u_exact, fp8, f"{what} block {b}", slack, check_fraction=False)
         differ += rb["differ"]
         n_slack += rb["slack"]
-    frac = differ / max(codes_g.size, 1)
-    assert frac <= TOL["fp8_frac"], f"{what}: {differ} of {codes_g.size} codes differ ({frac:.2e})"
-    assert boundary <= allowance_budget(r * nb), \
-        f"{what}: {boundary} of {r * nb} E8M0 scales differ inside the boundary window"
-    assert n_slack <= allowance_budget(codes_g.size), \
-        f"{what}: {n_slack} of {codes_g.size} codes pass only through the cancellation allowance"
-    return Report(boundary_blocks=boundary, differ=differ, slack=n_slack, blocks=r * nb)
+    rep = Report(boundary_blocks=boundary, differ=differ, slack=n_slack, blocks=r * nb, n=int(codes_g.size))
+    if not aggregate:
+        assert_mx_totals([rep], what)
+    return rep
+
+
+def assert_mx_totals(reports, what="mx"):
+    """The tensor-wide bounds of check_mx_rows over reports of pieces of one tensor."""
+    n = sum(r["n"] for r in reports)
+    blocks = sum(r["blocks"] for r in reports)
+    differ = sum(r["differ"] for r in reports)
+    boundary = sum(r["boundary_blocks"] for r in reports)
+    slack = sum(r["slack"] for r in reports)
+    frac = differ / max(n, 1)
+    assert frac <= TOL["fp8_frac"], f"{what}: {differ} of {n} codes differ ({frac:.2e})"
+    assert boundary <= allowance_budget(blocks), \
+        f"{what}: {boundary} of {blocks} E8M0 scales differ inside the boundary window"
+    assert slack <= allowance_budget(n), f"{what}: {slack} of {n} codes pass only through the cancellation allowance"
+    return Report(n=n, blocks=blocks, differ=differ, boundary_blocks=boundary, slack=slack)
+
+
+def assert_fp8_totals(reports, n, what="codes"):
+    """The tensor-wide bounds of check_fp8 over reports of n codes checked in pieces."""
+    differ = sum(r["differ"] for r in reports)
+    slack = sum(r["slack"] for r in reports)
+    assert differ / max(n, 1) <= TOL["fp8_frac"], f"{what}: {differ} of {n} codes differ"
+    assert slack <= allowance_budget(n), f"{what}: {slack} of {n} codes pass only through the cancellation allowance"
+    return Report(n=n, differ=differ, slack=slack)
+
+
+def assert_hp_totals(reports, what="y"):
+    """The tensor-wide cancellation bound of check_hp over reports of pieces of one tensor."""
+    n = sum(r["n"] for r in reports)
+    cancel = sum(r["cancellation"] for r in reports)
+    assert cancel <= allowance_budget(n), f"{what}: {cancel} of {n} elements pass only through the cancellation allowance"
+    return Report(n=n, cancellation=cancel, off_by_one=sum(r["off_by_one"] for r in reports))
 
 
 def half_ulp(v, dtype):

@@ -1,14 +1,20 @@
-"""GPU: the torch.autograd functions route to the same kernels as the direct calls.
+"""GPU: the torch.autograd functions route to the same kernels as the direct calls, and their
+results match the oracle.
 
 Each check is bit-exact against the direct ``fwd`` / ``bwd`` / ``bwd_add`` calls on the same
-inputs (those calls are pinned to the oracle by test_gpu_parity.py), plus a loose comparison
-with torch's own float32 autograd of the same formula as a plumbing check (shapes, which
-gradient goes where, zero-centred gamma, the residual branch).
+inputs, then against the oracle (y from the oracle's forward; dx, dgamma, dbeta from its
+backward at its own statistics, the end-to-end check of the GPU forward feeding the GPU
+backward), plus a loose comparison with torch's own float32 autograd of the same formula as a
+plumbing check (shapes, which gradient goes where, zero-centred gamma, the residual branch).
+[BwdAdd] "Implementation: NVIDIA TransformerEngine Ops Fused Backward Add RMSNorm", Usage and
+I/O Contract: the fused backward-add pattern (the residual branch's gradient added into dx).
 """
 import pytest
 import torch
 
+import checks
 import workloads
+from test_gpu_parity import bits, ln_terms, oracle_bwd, oracle_fwd
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +63,17 @@ def test_autograd_norm(norm, zc):
     if b is not None:
         assert torch.equal(b.grad, d["dbeta"])
 
+    # against the oracle: forward values and statistics, then the backward end to end
+    ref_f = oracle_fwd(c, norm, "bf16", "f32", zc)
+    checks.check_stats(None if f["mu"] is None else f["mu"].cpu().numpy(), f["rsigma"].cpu().numpy(),
+                       ref_f["mu"], ref_f["rsigma"])
+    checks.check_hp(bits(y.detach().view(rows, hidden)), ref_f["v"], "bf16", terms=ln_terms(c, ref_f, norm, zc=zc))
+    ref_b = oracle_bwd(c, norm, "bf16", "f32", zc, ref_f)
+    checks.check_dx(bits(x.grad.view(rows, hidden)), ref_b["dx"], "bf16")
+    checks.check_wgrad(g.grad.cpu().numpy(), ref_b["dgamma"])
+    if b is not None:
+        checks.check_wgrad(b.grad.cpu().numpy(), ref_b["dbeta"], what="dbeta")
+
     # plumbing against torch's float32 autograd (bf16 rounding of y and dx bounds the difference)
     xr = x.detach().clone().requires_grad_()
     gr = g.detach().clone().requires_grad_()
@@ -89,6 +106,13 @@ def test_autograd_rms_norm_residual(zc):
     assert torch.equal(y.detach().view(rows, hidden), f["y"])
     assert torch.equal(x.grad.view(rows, hidden), d["dx"])
     assert torch.equal(g.grad, d["dgamma"])
+
+    # against the oracle: dx = RMSNorm backward + residual gradient, and dgamma
+    ref_f = oracle_fwd(c, "rmsnorm", "bf16", "f32", zc)
+    checks.check_hp(bits(y.detach().view(rows, hidden)), ref_f["v"], "bf16")
+    ref_b = oracle_bwd(c, "rmsnorm", "bf16", "f32", zc, ref_f, add=True)
+    checks.check_dx(bits(x.grad.view(rows, hidden)), ref_b["dx"], "bf16")
+    checks.check_wgrad(g.grad.cpu().numpy(), ref_b["dgamma"])
 
     # only the norm output used: the plain backward, no residual term
     x.grad = None

@@ -596,15 +596,22 @@ def test_fwd_then_bwd_end_to_end():
 # ------------------------------------------------------------------------------ determinism
 
 def test_repeat_runs_are_bitwise_identical():
+    """Repeated calls give the same bytes: the band split (forced: its cross-workgroup exchange
+    of row partials through tagged words and tickets), the columnwise tile path, the single-pass
+    columnwise band kernel and the backward's fixed-order partial reduction."""
     case = workloads.small_case("layernorm", 500, 20480, "bf16", "f32", seed=8)
     dy, x, g, b = gpu(case, "dy", "x", "gamma", "beta")
     xs, dys, gs = x[:, :16384].contiguous(), dy[:, :16384].contiguous(), g[:16384].contiguous()
     outs = []
     for _ in range(3):
-        f = nf.fwd(x, g, b, norm="layernorm")                      # band split (20480 columns)
+        with env(NORMFP8_FORCE_BAND=1):
+            f = nf.fwd(x, g, b, norm="layernorm")                  # band split (20480 columns)
+        with env(NORMFP8_COL_KERNEL=0):
+            fb = nf.fwd(x, g, b, norm="layernorm", scaling="mxfp8", layout="rowwise_colwise")
         fc = nf.fwd(x, g, b, norm="layernorm", scaling="mxfp8", layout="rowwise_colwise")
         d = nf.bwd(dys, xs, f["mu"], f["rsigma"], gs, norm="layernorm")
-        outs.append([t.clone() for t in (f["y"], f["mu"], fc["y"], fc["y_colwise"], fc["colwise_scale_inv"],
+        outs.append([t.clone() for t in (f["y"], f["mu"], f["rsigma"], fb["y"], fb["y_colwise"], fb["rsigma"],
+                                          fc["y"], fc["y_colwise"], fc["colwise_scale_inv"],
                                           d["dx"], d["dgamma"], d["dbeta"])])
     for o in outs[1:]:
         for a, b_ in zip(outs[0], o):
