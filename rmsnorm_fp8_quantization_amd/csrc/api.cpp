@@ -66,7 +66,7 @@ constexpr int kKnobUnset = INT_MIN;
 const char *const kKnobNames[] = {"NORMFP8_FORCE_BAND",       "NORMFP8_ROW_CFG",      "NORMFP8_COL_KERNEL",
                                   "NORMFP8_DELAYED_TRANSPOSE", "NORMFP8_BAND_CFG",     "NORMFP8_BWD_CFG",
                                   "NORMFP8_ROW_OCC",           "NORMFP8_ROW_BALANCE",  "NORMFP8_TRANSPOSE_TC",
-                                  "NORMFP8_TRANSPOSE_RL",      "NORMFP8_BAND_CLASSES"};
+                                  "NORMFP8_TRANSPOSE_RL",      "NORMFP8_BAND_CLASSES", "NORMFP8_SPLIT"};
 enum Knob : int {
   K_FORCE_BAND = 0,
   K_ROW_CFG,
@@ -79,6 +79,7 @@ enum Knob : int {
   K_TRANSPOSE_TC,
   K_TRANSPOSE_RL,
   K_BAND_CLASSES,
+  K_SPLIT,
   K_NKNOBS
 };
 static_assert(sizeof(kKnobNames) / sizeof(kKnobNames[0]) == K_NKNOBS, "knob table");
@@ -168,7 +169,14 @@ struct FwdPlan {
   bool scales_padded = false;  // MXFP8 E8M0 grids padded (block dimension to 4, the other to 128)
   bool tr = false;    // delayed scaling, rowwise + columnwise: row kernel, then a byte transpose
   bool gen = false;   // general kernels: hidden not a multiple of 8 (or, at launch, unaligned tensors)
+  bool split = false; // long rows, no FP8 epilogue: the split kernel (S slices per row, weights in LDS)
 };
+
+// rows longer than the row layouts (65536 elements) without an FP8 epilogue go to the split
+// kernel (LayerNorm bf16 682 x 98304: 204 -> 79 us, RMSNorm 512 x 131072: 105 -> 63 us against
+// the band kernel); up to 65536 the one-workgroup-per-row layout is faster (LayerNorm
+// 1024 x 65536: 68 against 72 us; RMSNorm 52 against 63 us)
+constexpr int64_t kSplitMinHidden = 65536 + 8;
 
 int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
              int scaling, int qlayout, int cu_margin, FwdPlan *pl) {
@@ -293,14 +301,32 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     }
   }
 
-  // workspace: header when the launch coordinates workgroups, then band partials
-  const bool header = pl->mode == MODE_DELAYED || (pl->band && pl->S > 1);
+  // long rows without an FP8 epilogue: the split kernel (NORMFP8_SPLIT=0 keeps the row / band
+  // layouts, =1 takes the split kernel for any row it covers)
+  {
+    const int force = knob(K_SPLIT, -1);
+    const int64_t S = cdiv(hidden, kSplitCols);
+    const bool fits = pl->mode == MODE_PLAIN && !pl->colwise && !pl->gen && !force_band && S <= kSplitMaxSlices;
+    if (fits && (force == 1 || (force < 0 && hidden >= kSplitMinHidden))) {
+      pl->split = true;
+      pl->band = pl->col = false;
+      pl->S = (int)S;
+    }
+  }
+
+  // workspace: header when the launch coordinates workgroups, then band or split partials
+  const bool header = pl->mode == MODE_DELAYED || (pl->band && pl->S > 1) || pl->split;
   if (pl->gen) pl->cfg = 0;
   size_t ws = header ? (size_t)kWsHeaderBytes : 0;
   if (pl->band && pl->S > 1) {
     pl->partial_off = ws;
     const int nv = norm_type == NORM_LAYERNORM ? 3 : 1;  // (mean, M2, shift) or the sum of squares
     ws += round_up((size_t)pl->bands * pl->S * pl->tile_rows * nv * sizeof(uint64_t), 256);
+  }
+  if (pl->split) {
+    pl->partial_off = ws;
+    const int nv = norm_type == NORM_LAYERNORM ? 3 : 1;
+    ws += round_up((size_t)rows * pl->S * nv * sizeof(uint64_t), 256);
   }
   // row statistics of a columnwise request (two-pass paths; sized for every columnwise request,
   // since unaligned tensors send any request to the general kernels at launch)
@@ -595,6 +621,27 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
       rc = launch(fc, dim3((unsigned)g2), dim3(64), &tp, st);
       if (rc) return rc;
     }
+    return ok();
+  }
+  if (pl.split) {
+    const void *fn = fwd_split_kernel_ptr(norm_type, in_dtype);
+    if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no split kernel for this combination");
+    int occ = 1;
+    rc = occupancy(fn, kSplitThreads, &occ);
+    if (rc) return rc;
+    int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
+    if (cap > kMaxGrid) cap = kMaxGrid;
+    int64_t groups = cap / pl.S;
+    if (groups > rows) groups = rows;
+    if (groups < 1)
+      return fail(NORM_ERR_UNSUPPORTED, "cu_margin %d leaves fewer than the %d resident workgroups a split row needs",
+                  cu_margin, pl.S);
+    FwdSplitParams sp{};
+    sp.f = f;
+    sp.partials = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + pl.partial_off);
+    sp.S = pl.S;
+    rc = launch(fn, dim3((unsigned)(groups * pl.S)), dim3(kSplitThreads), &sp, st);
+    if (rc) return rc;
     return ok();
   }
   if (!pl.band && !pl.col) {

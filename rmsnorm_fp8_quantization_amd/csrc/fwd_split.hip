@@ -1,0 +1,299 @@
+// fwd_split.hip -- LayerNorm / RMSNorm forward for long rows, each row split over S workgroups
+// whose weight slices stay in LDS.
+//
+// [XLA-Norm] = "Implementation: NVIDIA TransformerEngine JAX XLA Normalization";
+// [NVRTC-PR] = "Migrate norms and softmax kernels to NVRTC" (TransformerEngine pull request).
+// [NVRTC-PR] Greptile Summary and Flowchart: rows too long for one CTA are split over several
+// CTAs that combine their partial statistics through a workspace. [XLA-Norm] I/O Contract: the
+// forward's outputs y, mu (LayerNorm) and rsigma.
+//
+// A row of H elements is cut into S = ceil(H / 16384) slices. A workgroup of 16 waves owns one
+// slice of every row of its row group: it stages the slice's gamma / beta (float32, 1 + gamma
+// when zero-centred) in LDS once -- 128 KB for LayerNorm -- and then walks its rows, so no
+// weight is read again from the caches per row (a 65536-element row re-read 512 KB of weights
+// per row through the L2 in the one-workgroup-per-row layout). Lane t holds two 16-byte strips
+// of the slice: columns 8 (t + 1024 k), k < 2.
+//
+// Per row: every wave reduces its 1024 elements (LayerNorm: deviations from the wave's plain
+// mean estimate, so that a large common part of the row costs no precision), the 16 wave
+// partials are merged through LDS in wave order, and the slice's partial is published to the
+// workspace as tagged 64-bit words {value, launch tag}. Each workgroup then polls the S slices'
+// words of the row and merges them in slice order, so all S workgroups obtain identical
+// statistics. Four rows are in flight: row j + 3 is loading and row j + 2 publishes its partial
+// while row j is normalised with its partners' words, which were published two rows earlier and
+// loaded one row earlier, so the exchange overlaps the loads of the next rows.
+//
+// Group membership comes from tickets taken at start (group = ticket / S, slice = ticket % S):
+// every ticket is held by a running workgroup, so a workgroup only waits on workgroups that are
+// running or can still start; every wait has the 2 s limit of wait_tagged. The workgroup that
+// finishes last re-zeroes the ticket counter and advances the launch epoch.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace nf8 {
+
+template <int NORM, class IN>
+__global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(FwdSplitParams sp) {
+  constexpr int NT = kSplitThreads;
+  constexpr int KC = kSplitStrips;
+  constexpr int W = kSplitCols;                     // slice width (elements)
+  constexpr int NW = NORM == NT_LAYERNORM ? 2 : 1;  // weight arrays
+  constexpr int NV = NORM == NT_LAYERNORM ? 3 : 1;  // tagged words per slice partial
+  constexpr int NWAVE = NT / 64;
+  const FwdRowParams &p = sp.f;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t H = p.hidden;
+  const int64_t N = p.rows;
+  const int S = sp.S;
+
+  __shared__ float wlds[NW * W];
+  __shared__ ShiftedStats wpart[2][NWAVE];
+  __shared__ uint32_t s_ticket, s_epoch, s_last;
+
+  if (tid == 0) {
+    s_epoch = ld_dev_u32(p.ws + kWsEpoch);
+    s_ticket = add_dev(p.ws + kWsTicket0, 1u);
+  }
+  __syncthreads();
+  const uint32_t tag = epoch_tag(s_epoch);
+  const int ticket = (int)s_ticket;
+  const int group = ticket / S;
+  const int slice = ticket - group * S;
+  const int ngroups = (int)gridDim.x / S;
+  const int64_t c0 = (int64_t)slice * W;
+  const int cols = (int)(H - c0 < W ? H - c0 : W);  // columns of this slice
+
+  // ---- the slice's weights, once
+  for (int c = 8 * tid; c < cols; c += 8 * NT) {
+    float w[8];
+    load_w8(w, p.gamma, c0 + c, p.w_dtype);
+    if (p.zero_centered) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] += 1.0f;
+    }
+    float4 *d = reinterpret_cast<float4 *>(wlds + c);
+    d[0] = make_float4(w[0], w[1], w[2], w[3]);
+    d[1] = make_float4(w[4], w[5], w[6], w[7]);
+    if constexpr (NORM == NT_LAYERNORM) {
+      load_w8(w, p.beta, c0 + c, p.w_dtype);
+      float4 *e = reinterpret_cast<float4 *>(wlds + W + c);
+      e[0] = make_float4(w[0], w[1], w[2], w[3]);
+      e[1] = make_float4(w[4], w[5], w[6], w[7]);
+    }
+  }
+
+  bool cv[KC];
+  float n_in = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    cv[k] = 8 * (tid + NT * k) < cols;
+    n_in += cv[k] ? 8.0f : 0.0f;
+  }
+  const float n_w = wave_sum(n_in);  // this wave's elements of the slice
+  const float inv_nw = 1.0f / fmaxf(n_w, 1.0f);
+  const float inv_h = 1.0f / (float)H;
+  uint32_t *const err = p.ws + kWsError;
+  __syncthreads();  // weights staged
+
+  // rows of this group: group, group + ngroups, ... (nr of them)
+  const int64_t nr = group < N ? (N - group + ngroups - 1) / ngroups : 0;
+  auto row_of = [&](int64_t j) { return group + j * ngroups; };
+
+  typedef Strip<IN> RowBuf[KC];
+  // unconditional loads: a row past the group's last reads row 0, a strip past the slice reads
+  // the slice's first strip (masked where used)
+  auto load_row = [&](RowBuf &b, int64_t j) {
+    const int64_t r = j < nr ? row_of(j) : 0;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) load_strip<IN>(b[k], p.x, r * H + c0 + (cv[k] ? 8 * (tid + NT * k) : 0));
+  };
+  auto part_of = [&](int64_t r) { return sp.partials + r * (int64_t)S * NV; };
+
+  // ---- statistics of row j's slice, published (every wave takes part: one barrier)
+  auto stats_publish = [&](RowBuf &b, int64_t j) {
+    if (cols != W) {
+#pragma unroll
+      for (int k = 0; k < KC; ++k) mask_strip<IN>(b[k], cv[k]);
+    }
+    ShiftedStats ws{Stats{0.0f, 0.0f, 0.0f}, 0.0f};
+    if constexpr (NORM == NT_LAYERNORM) {
+      float sa = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float xv[8];
+        strip_to_f32<IN>(b[k], xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sa += xv[i];
+      }
+      // the wave's shift, rounded once (readfirstlane keeps a product from being fused into
+      // each x - K)
+      const float K = first_lane(wave_sum(sa) * inv_nw);
+#pragma unroll
+      for (int k = 0; k < KC; ++k) opaque<IN>(b[k]);  // converted again, not kept as floats
+      float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float xv[8];
+        strip_to_f32<IN>(b[k], xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float d = cv[k] ? xv[i] - K : 0.0f;
+          s1 += d;
+          s2 = fmaf(d, d, s2);
+        }
+      }
+      const float t1 = wave_sum(s1), t2 = wave_sum(s2);
+      const float m = t1 * inv_nw;
+      ws = ShiftedStats{Stats{n_w, m, fmaxf(fmaf(-t1, m, t2), 0.0f)}, K};
+    } else {
+      float q = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float xv[8];
+        strip_to_f32<IN>(b[k], xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q = fmaf(xv[i], xv[i], q);  // masked strips are zero
+      }
+      ws.s.m2 = wave_sum(q);
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) opaque<IN>(b[k]);  // (the row is converted again in finish)
+    if (lane == 0) wpart[j & 1][wave] = ws;
+    __syncthreads();
+    if (wave == 0 && j < nr) {
+      Stats st = wpart[j & 1][0].s;
+      const float k0 = wpart[j & 1][0].k;
+#pragma unroll 1
+      for (int w = 1; w < NWAVE; ++w) {  // (not unrolled: sixteen partials read ahead would take 64 registers)
+        const ShiftedStats o = wpart[j & 1][w];
+        if constexpr (NORM == NT_LAYERNORM) st = chan_merge(st, in_frame(o, k0));
+        else st.m2 += o.s.m2;
+      }
+      uint64_t *dst = part_of(row_of(j)) + slice * NV;
+      if constexpr (NORM == NT_LAYERNORM) {
+        const float v = lane == 0 ? st.mean : (lane == 1 ? st.m2 : k0);
+        if (lane < NV) st_dev64(dst + lane, tagged(v, tag));
+      } else {
+        if (lane == 0) st_dev64(dst, tagged(st.m2, tag));
+      }
+    }
+  };
+
+  // The S slices' words of a row are loaded one row ahead of their use, before the stores of
+  // the row in between: loads and stores retire in issue order, so a word loaded after a row's
+  // stores (or after the next row's prefetch) could only be used once those had completed.
+  auto poll_issue = [&](int64_t j) -> uint64_t {
+    const uint64_t *pr = part_of(j < nr ? row_of(j) : 0);
+    return lane < S * NV ? ld_dev64(pr + lane) : 0ull;
+  };
+
+  // ---- row j: the S partials (loaded as pv), merged in slice order; then the next row's words
+  // are loaded, and the slice is normalised and stored
+  auto finish = [&](RowBuf &b, int64_t j, uint64_t &pv) {
+    const int64_t r = row_of(j);
+    float v = __uint_as_float((uint32_t)pv);
+    if (lane < S * NV && (uint32_t)(pv >> 32) != tag) v = wait_tagged(part_of(r) + lane, tag, err);
+    float mu = 0.0f, rs;
+    if constexpr (NORM == NT_LAYERNORM) {
+      auto word = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+      const float k0 = word(2);
+      Stats acc{(float)(H < W ? H : W), word(0), word(1)};
+      for (int s = 1; s < S; ++s) {
+        const int64_t left = H - (int64_t)s * W;
+        const ShiftedStats o{Stats{(float)(left < W ? left : W), word(3 * s), word(3 * s + 1)}, word(3 * s + 2)};
+        acc = chan_merge(acc, in_frame(o, k0));
+      }
+      mu = k0 + acc.mean;
+      rs = __builtin_amdgcn_rsqf(acc.m2 * inv_h + p.eps);
+    } else {
+      float q = 0.0f;
+      for (int s = 0; s < S; ++s)
+        q += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), s));
+      rs = __builtin_amdgcn_rsqf(q * inv_h + p.eps);
+    }
+    pv = poll_issue(j + 1);
+    if (slice == 0 && tid == 0) {
+      if (p.rsigma) p.rsigma[r] = rs;
+      if constexpr (NORM == NT_LAYERNORM) {
+        if (p.mu) p.mu[r] = mu;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int c = 8 * (tid + NT * k);
+      float xv[8], y[8];
+      strip_to_f32<IN>(b[k], xv);
+      const float4 *g4 = reinterpret_cast<const float4 *>(wlds + c);
+      const float4 ga = g4[0], gb = g4[1];
+      const float gk[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      if constexpr (NORM == NT_LAYERNORM) {
+        const float4 *b4 = reinterpret_cast<const float4 *>(wlds + W + c);
+        const float4 ba = b4[0], bb = b4[1];
+        const float bk[8] = {ba.x, ba.y, ba.z, ba.w, bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = fmaf((xv[i] - mu) * rs, gk[i], bk[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = (xv[i] * rs) * gk[i];
+      }
+      if (cv[k]) store_out8(p.y, r * H + c0 + c, y, p.out_dtype);
+      __builtin_amdgcn_sched_barrier(0);  // one strip's weights and values live at a time
+    }
+  };
+
+  // three row buffers in turn: row j + 2 loads while row j + 1 is reduced and published and
+  // row j finishes
+  // four row buffers in turn: row j + 3 loads while row j + 2 is reduced and published and row
+  // j finishes with the words loaded one row earlier (two rows after their publication)
+  RowBuf A, B, C, D;
+  load_row(A, 0);
+  load_row(B, 1);
+  load_row(C, 2);
+  stats_publish(A, 0);
+  stats_publish(B, 1);
+  uint64_t pv = poll_issue(0);
+  for (int64_t j = 0; j < nr; j += 4) {
+    load_row(D, j + 3);
+    stats_publish(C, j + 2);
+    finish(A, j, pv);
+    if (j + 1 >= nr) break;
+    load_row(A, j + 4);
+    stats_publish(D, j + 3);
+    finish(B, j + 1, pv);
+    if (j + 2 >= nr) break;
+    load_row(B, j + 5);
+    stats_publish(A, j + 4);
+    finish(C, j + 2, pv);
+    if (j + 3 >= nr) break;
+    load_row(C, j + 6);
+    stats_publish(B, j + 5);
+    finish(D, j + 3, pv);
+  }
+
+  // ---- end of launch: the last workgroup re-zeroes the ticket counter and advances the epoch
+  vmem_drain();
+  if (finish_workgroup(p.ws, &s_last)) {
+    if (tid == 0) xchg_dev(p.ws + kWsTicket0, 0u);
+    vmem_drain();
+    __syncthreads();
+    reset_completion(p.ws);
+  }
+}
+
+template <int NORM>
+static const void *pick_split_in(int in_dtype) {
+  switch (in_dtype) {
+    case DT_F32: return (const void *)fwd_split_kernel<NORM, F32>;
+    case DT_BF16: return (const void *)fwd_split_kernel<NORM, BF16>;
+    case DT_F16: return (const void *)fwd_split_kernel<NORM, F16>;
+    default: return nullptr;
+  }
+}
+
+const void *fwd_split_kernel_ptr(int norm, int in_dtype) {
+  return norm == NT_LAYERNORM ? pick_split_in<NT_LAYERNORM>(in_dtype) : pick_split_in<NT_RMSNORM>(in_dtype);
+}
+
+}  // namespace nf8

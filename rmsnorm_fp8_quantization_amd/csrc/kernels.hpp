@@ -72,6 +72,12 @@ constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1, 4}, {4, 1, 2}, {4, 2, 2}, {8, 
                                            {16, 2, 1}, {8, 1, 1}, {16, 1, 1}, {4, 4, 1},
                                            {2, 1, 1}, {4, 1, 1}, {4, 2, 1}, {8, 3, 1}};
 
+// ---- forward split kernel: 16 waves, two 16-byte strips per lane: a 16384-column slice
+constexpr int kSplitThreads = 1024;
+constexpr int kSplitStrips = 2;
+constexpr int kSplitCols = 8 * kSplitThreads * kSplitStrips;
+constexpr int kSplitMaxSlices = 8;  // rows up to 131072 elements
+
 // ---- forward tile kernel (second pass of a columnwise output): 8 waves, 128 x 128 tiles
 constexpr int kColTileRows = 128;
 constexpr int kColTileCols = 128;
@@ -79,6 +85,7 @@ constexpr int kColThreads = 4 * kColTileRows;  // 16 rows per wave
 
 const void *fwd_row_kernel_ptr(int norm, int in_dtype, int mode, int cfg);
 const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg);
+const void *fwd_split_kernel_ptr(int norm, int in_dtype);
 const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor);
 // tiles of 32 * rows_per_lane rows x 256 columns (rows_per_lane 4 or 8), or of 512 rows x 128
 // columns (tile_cols 128, rows_per_lane 8)

@@ -91,6 +91,16 @@ struct FwdBandParams {
   int write_row;         // rowwise output requested
 };
 
+// ---- forward split kernel (long rows) -------------------------------------------------------
+// S workgroups per row group, each holding one 16384-column slice of every row of the group and
+// that slice's weights in LDS; per row the slices exchange tagged partial statistics
+// (LayerNorm: mean and M2 relative to a shift, and the shift; RMSNorm: the sum of squares).
+struct FwdSplitParams {
+  FwdRowParams f;        // y = the output
+  uint64_t *partials;    // [rows, S, NV] tagged slice partials (NV = 3 LayerNorm, 1 RMSNorm)
+  int S;                 // slices per row
+};
+
 // ---- forward tile kernel (second pass of a columnwise output) -------------------------------
 // Independent tiles of 128 rows x 128 columns, each normalised with the row statistics the
 // first pass (row kernel, MODE_STATS) wrote to st_mu / st_rs.

@@ -593,6 +593,45 @@ def test_fwd_then_bwd_end_to_end():
     checks.check_wgrad(out["dgamma"].cpu().numpy(), ref["dgamma"])
 
 
+# ------------------------------------------------------------------------------ split rows
+
+SPLIT_SHAPES = [(3, 8), (5, 4096), (37, 16384), (9, 16392), (300, 40000), (2, 65536), (70, 65536),
+                (4, 131072), (1, 98304)]
+
+
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("in_dt", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("rows,hidden", SPLIT_SHAPES)
+def test_fwd_split_rows(norm, in_dt, rows, hidden):
+    """The split kernel (S = ceil(hidden / 16384) workgroups per row, weight slices in LDS,
+    tagged partial exchange), forced on every shape: one to eight slices, ragged last slices,
+    fewer rows than row groups."""
+    case = workloads.small_case(norm, rows, hidden, in_dt, "f32", seed=rows + hidden + 11)
+    ref = oracle_fwd(case, norm, in_dt, "f32", False)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    with env(NORMFP8_SPLIT=1):
+        out = nf.fwd(x, g, b, norm=norm, eps=EPS)
+    checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
+                       out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+    checks.check_hp(bits(out["y"]), ref["v"], in_dt, terms=ln_terms(case, ref, norm))
+    assert_ws_clean()
+
+
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+def test_fwd_split_zero_centered_bf16_weights_and_margin(norm):
+    rows, hidden = 33, 49152
+    case = workloads.small_case(norm, rows, hidden, "bf16", "bf16", seed=5, zero_centered_gamma=True)
+    ref = oracle_fwd(case, norm, "bf16", "bf16", True)
+    x, g, b = gpu(case, "x", "gamma", "beta")
+    for margin in (0, 200, 250):
+        with env(NORMFP8_SPLIT=1):
+            out = nf.fwd(x, g, b, norm=norm, eps=EPS, zero_centered_gamma=True, cu_margin=margin)
+        checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
+                           out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
+        checks.check_hp(bits(out["y"]), ref["v"], "bf16", terms=ln_terms(case, ref, norm, "bf16", zc=True))
+    assert_ws_clean()
+
+
 # ------------------------------------------------------------------------------ determinism
 
 def test_repeat_runs_are_bitwise_identical():
@@ -604,13 +643,16 @@ def test_repeat_runs_are_bitwise_identical():
     xs, dys, gs = x[:, :16384].contiguous(), dy[:, :16384].contiguous(), g[:16384].contiguous()
     outs = []
     for _ in range(3):
-        with env(NORMFP8_FORCE_BAND=1):
+        with env(NORMFP8_FORCE_BAND=1, NORMFP8_SPLIT=0):
             f = nf.fwd(x, g, b, norm="layernorm")                  # band split (20480 columns)
+        with env(NORMFP8_SPLIT=1):
+            fs = nf.fwd(x, g, b, norm="layernorm")                 # split kernel (two slices)
         with env(NORMFP8_COL_KERNEL=0):
             fb = nf.fwd(x, g, b, norm="layernorm", scaling="mxfp8", layout="rowwise_colwise")
         fc = nf.fwd(x, g, b, norm="layernorm", scaling="mxfp8", layout="rowwise_colwise")
         d = nf.bwd(dys, xs, f["mu"], f["rsigma"], gs, norm="layernorm")
-        outs.append([t.clone() for t in (f["y"], f["mu"], f["rsigma"], fb["y"], fb["y_colwise"], fb["rsigma"],
+        outs.append([t.clone() for t in (f["y"], f["mu"], f["rsigma"], fs["y"], fs["mu"], fs["rsigma"],
+                                          fb["y"], fb["y_colwise"], fb["rsigma"],
                                           fc["y"], fc["y_colwise"], fc["colwise_scale_inv"],
                                           d["dx"], d["dgamma"], d["dbeta"])])
     for o in outs[1:]:
