@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnormfp8.so")
-SOURCES = ["api.cpp", "fwd_row.hip", "fwd_band.hip", "fwd_col.hip", "bwd.hip", "gen.hip", "noalloc.hip", "fwd_split.hip"]
+SOURCES = ["api.cpp", "fwd_row.hip", "fwd_band.hip", "fwd_col.hip", "bwd.hip", "gen.hip", "noalloc.hip", "fwd_split.hip", "fwd_colx.hip"]
 ARCH = "gfx950"
 
 

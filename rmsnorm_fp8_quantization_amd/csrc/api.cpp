@@ -66,7 +66,7 @@ constexpr int kKnobUnset = INT_MIN;
 const char *const kKnobNames[] = {"NORMFP8_FORCE_BAND",       "NORMFP8_ROW_CFG",      "NORMFP8_COL_KERNEL",
                                   "NORMFP8_DELAYED_TRANSPOSE", "NORMFP8_BAND_CFG",     "NORMFP8_BWD_CFG",
                                   "NORMFP8_ROW_OCC",           "NORMFP8_ROW_BALANCE",  "NORMFP8_TRANSPOSE_TC",
-                                  "NORMFP8_TRANSPOSE_RL",      "NORMFP8_BAND_CLASSES", "NORMFP8_SPLIT"};
+                                  "NORMFP8_TRANSPOSE_RL",      "NORMFP8_BAND_CLASSES", "NORMFP8_SPLIT", "NORMFP8_COLX"};
 enum Knob : int {
   K_FORCE_BAND = 0,
   K_ROW_CFG,
@@ -80,6 +80,7 @@ enum Knob : int {
   K_TRANSPOSE_RL,
   K_BAND_CLASSES,
   K_SPLIT,
+  K_COLX,
   K_NKNOBS
 };
 static_assert(sizeof(kKnobNames) / sizeof(kKnobNames[0]) == K_NKNOBS, "knob table");
@@ -164,12 +165,14 @@ struct FwdPlan {
   int64_t bands = 0;
   size_t ws_bytes = 0;
   size_t partial_off = 0;
+  size_t colx_off = 0;   // single-pass columnwise partials
   size_t stats_off = 0;  // two-pass path: mu / rsigma when the caller passes none
   bool col_rowmajor = false;
   bool scales_padded = false;  // MXFP8 E8M0 grids padded (block dimension to 4, the other to 128)
   bool tr = false;    // delayed scaling, rowwise + columnwise: row kernel, then a byte transpose
   bool gen = false;   // general kernels: hidden not a multiple of 8 (or, at launch, unaligned tensors)
   bool split = false; // long rows, no FP8 epilogue: the split kernel (S slices per row, weights in LDS)
+  bool colx = false;  // RMSNorm FP8 with a columnwise output: the single-pass band-exchange kernel
 };
 
 // rows longer than the row layouts (65536 elements) without an FP8 epilogue go to the split
@@ -314,8 +317,21 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     }
   }
 
+  // RMSNorm FP8 with a transposed columnwise output, hidden a multiple of 512 and rows a
+  // multiple of 128: one pass over x, the bands' row sums exchanged between the slices
+  // (NORMFP8_COLX=0 keeps the two-pass routes)
+  // (float32 input keeps the two-pass routes: two bands of it would fill the registers)
+  if (norm_type == NORM_RMSNORM && pl->colwise && !col_rowmajor && !pl->gen && pl->mode != MODE_PLAIN &&
+      in_dtype != DT_F32 &&
+      hidden % kColxCols == 0 && rows > 0 && rows % kColxRows == 0 && rows * (int64_t)kColxRows < (1ll << 32) &&
+      (int64_t)kColxRows * hidden * 2 < (1ll << 32) &&
+      knob(K_COLX, 1) != 0) {
+    pl->colx = true;
+    pl->S = (int)(hidden / kColxCols);
+  }
+
   // workspace: header when the launch coordinates workgroups, then band or split partials
-  const bool header = pl->mode == MODE_DELAYED || (pl->band && pl->S > 1) || pl->split;
+  const bool header = pl->mode == MODE_DELAYED || (pl->band && pl->S > 1) || pl->split || pl->colx;
   if (pl->gen) pl->cfg = 0;
   size_t ws = header ? (size_t)kWsHeaderBytes : 0;
   if (pl->band && pl->S > 1) {
@@ -327,6 +343,10 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     pl->partial_off = ws;
     const int nv = norm_type == NORM_LAYERNORM ? 3 : 1;
     ws += round_up((size_t)rows * pl->S * nv * sizeof(uint64_t), 256);
+  }
+  if (pl->colx) {
+    pl->colx_off = ws;
+    ws += round_up((size_t)rows * pl->S * sizeof(uint64_t), 256);
   }
   // row statistics of a columnwise request (two-pass paths; sized for every columnwise request,
   // since unaligned tensors send any request to the general kernels at launch)
@@ -643,6 +663,37 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     rc = launch(fn, dim3((unsigned)(groups * pl.S)), dim3(kSplitThreads), &sp, st);
     if (rc) return rc;
     return ok();
+  }
+  if (pl.colx) {
+    // (the two-pass routes serve what this kernel cannot: scale grids not 16 / 4-byte aligned, or
+    // a CU margin that leaves fewer resident workgroups than one band's slices)
+    const void *fn = fwd_colx_kernel_ptr(in_dtype, pl.mode);
+    int occ = 1;
+    if (fn) {
+      rc = occupancy(fn, kColxThreads, &occ);
+      if (rc) return rc;
+    }
+    int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
+    if (cap > kMaxGrid) cap = kMaxGrid;
+    int64_t groups = cap / pl.S;
+    const int64_t nbands = rows / kColxRows;
+    if (groups > nbands) groups = nbands;
+    const bool scales_ok = pl.mode != MODE_MX || ((!pl.rowwise || aligned16(scale_inv)) && aligned_to(colwise_scale_inv, 4));
+    if (fn && groups >= 1 && scales_ok) {
+      FwdColxParams cp{};
+      cp.f = f;
+      cp.y_col = y_colwise;
+      cp.col_scale_inv = colwise_scale_inv;
+      cp.partials = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + pl.colx_off);
+      cp.mx_col_ld = col_ld;
+      cp.S = pl.S;
+      cp.write_row = pl.rowwise ? 1 : 0;
+      if (!pl.rowwise) cp.f.y = nullptr;
+      rc = launch(fn, dim3((unsigned)(groups * pl.S)), dim3(kColxThreads), &cp, st);
+      if (rc) return rc;
+      return ok();
+    }
+    // otherwise the route planned without it
   }
   if (!pl.band && !pl.col) {
     rc = launch_rows(f, pl.mode);

@@ -78,6 +78,11 @@ constexpr int kSplitStrips = 2;
 constexpr int kSplitCols = 8 * kSplitThreads * kSplitStrips;
 constexpr int kSplitMaxSlices = 8;  // rows up to 131072 elements
 
+// ---- single-pass columnwise kernel: 8 waves, 128-row bands of 512-column slices
+constexpr int kColxThreads = 512;
+constexpr int kColxCols = 512;
+constexpr int kColxRows = 128;
+
 // ---- forward tile kernel (second pass of a columnwise output): 8 waves, 128 x 128 tiles
 constexpr int kColTileRows = 128;
 constexpr int kColTileCols = 128;
@@ -86,6 +91,7 @@ constexpr int kColThreads = 4 * kColTileRows;  // 16 rows per wave
 const void *fwd_row_kernel_ptr(int norm, int in_dtype, int mode, int cfg);
 const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg);
 const void *fwd_split_kernel_ptr(int norm, int in_dtype);
+const void *fwd_colx_kernel_ptr(int in_dtype, int mode);  // RMSNorm only
 const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor);
 // tiles of 32 * rows_per_lane rows x 256 columns (rows_per_lane 4 or 8), or of 512 rows x 128
 // columns (tile_cols 128, rows_per_lane 8)

@@ -101,6 +101,19 @@ struct FwdSplitParams {
   int S;                 // slices per row
 };
 
+// ---- forward single-pass columnwise kernel (RMSNorm, FP8) ------------------------------------
+// Workgroups own 512-column slices and walk down 128-row bands, exchanging the bands' row sums
+// of squares (one tagged word per row and slice) and writing rowwise and columnwise codes.
+struct FwdColxParams {
+  FwdRowParams f;        // y = rowwise codes (when write_row), scale_inv = rowwise scales
+  void *y_col;           // [hidden, rows] columnwise codes
+  void *col_scale_inv;   // delayed: float32[1]; MX: uint8 [hidden, rows/32] (row stride mx_col_ld)
+  uint64_t *partials;    // [rows / 128, S, 128] tagged slice partials
+  int64_t mx_col_ld;
+  int S;                 // slices per band (hidden / 512)
+  int write_row;
+};
+
 // ---- forward tile kernel (second pass of a columnwise output) -------------------------------
 // Independent tiles of 128 rows x 128 columns, each normalised with the row statistics the
 // first pass (row kernel, MODE_STATS) wrote to st_mu / st_rs.

@@ -632,6 +632,123 @@ def test_fwd_split_zero_centered_bf16_weights_and_margin(norm):
     assert_ws_clean()
 
 
+# ------------------------------------------------------------------------------ single-pass columnwise
+
+# (rows, hidden, cu_margin): 1 to 24 slices of 512 columns; margins that leave one group of
+# slices walking every band (an odd band count ends the two-band pipeline on its first half)
+COLX_SHAPES = [(128, 512, 0), (256, 1536, 0), (384, 4096, 0), (128, 12288, 0), (1024, 2048, 250),
+               (640, 8192, 240), (768, 4096, 0), (1152, 1024, 254)]
+
+
+def _colx_planned(rows, hidden, in_dt, scaling, layout, margin):
+    """The single-pass kernel's row partials (rows x slices tagged words) are in the workspace
+    plan when it is chosen."""
+    kw = dict(rows=rows, hidden=hidden, in_dtype=TDT[in_dt], w_dtype=torch.float32, out_code=nf._lib.NORM_FP8_E4M3,
+              norm="rmsnorm", scaling=scaling, layout=layout, cu_margin=margin)
+    with env(NORMFP8_COLX=1):
+        on = nf.fwd_workspace_size(**kw)
+    with env(NORMFP8_COLX=0):
+        off = nf.fwd_workspace_size(**kw)
+    return on >= off + rows * (hidden // 512) * 8
+
+
+def _colx_check(case, out, scaling, fp8, layout, in_dt="bf16", w_dt="f32", zc=False, scale=None):
+    ref = oracle_fwd(case, "rmsnorm", in_dt, w_dt, zc)
+    if scaling == "delayed":
+        got = {"y": bits(out["y"]) if out["y"] is not None else None, "y_colwise": bits(out["y_colwise"]),
+               "scale_inv": out["scale_inv"].item() if out["scale_inv"] is not None else None,
+               "colwise_scale_inv": out["colwise_scale_inv"].item(), "amax": out["amax"].item()}
+        checks.check_delayed(got, ref["v"], scale, 0.25, fp8, rowwise=layout != "colwise", colwise=True)
+    else:
+        rule = "ceil" if scaling == "mxfp8_ceil" else "floor"
+        if layout != "colwise":
+            checks.check_mx_rows(bits(out["y"]), bits(out["scale_inv"]), ref["v"], fp8, "mx rowwise", rule=rule)
+        checks.check_mx_rows(bits(out["y_colwise"]), bits(out["colwise_scale_inv"]),
+                             np.ascontiguousarray(ref["v"].T), fp8, "mx colwise", rule=rule)
+    checks.check_stats(None, out["rsigma"].cpu().numpy(), None, ref["rsigma"])
+
+
+def _colx_kw(case, scaling, fp8, ref_max):
+    if scaling != "delayed":
+        return {"scaling": scaling, "fp8": fp8}, None
+    top = F.E4M3.max_finite if fp8 == "e4m3" else F.E5M2.max_finite
+    scale = float(np.float32(top) / np.float32(ref_max / 4))    # a quarter of the range saturates
+    return {"scaling": "delayed", "fp8": fp8, "scale": torch.tensor([scale], device="cuda"),
+            "amax": torch.tensor([0.25], device="cuda")}, scale
+
+
+@pytest.mark.parametrize("scaling", ["delayed", "mxfp8", "mxfp8_ceil"])
+@pytest.mark.parametrize("layout", ["rowwise_colwise", "colwise"])
+@pytest.mark.parametrize("rows,hidden,margin", COLX_SHAPES)
+def test_fwd_colx(scaling, layout, rows, hidden, margin):
+    """RMSNorm with a columnwise FP8 output in one pass over x (bands of 128 rows, slices of 512
+    columns exchanging row sums of squares), forced, against the oracle."""
+    case = workloads.small_case("rmsnorm", rows, hidden, "bf16", "f32", seed=rows * 7 + hidden + margin)
+    xh = case["x"].float()
+    xh[::5, ::11] *= 16.0                        # outliers: saturated codes, spread block scales
+    case["x"] = xh.to(torch.bfloat16)
+    assert _colx_planned(rows, hidden, "bf16", scaling, layout, margin)
+    ref_max = float(np.max(np.abs(oracle_fwd(case, "rmsnorm", "bf16", "f32", False)["v"])))
+    kw, scale = _colx_kw(case, scaling, "e4m3", ref_max)
+    x, g = gpu(case, "x", "gamma")
+    with env(NORMFP8_COLX=1):
+        out = nf.fwd(x, g, None, norm="rmsnorm", eps=EPS, layout=layout, cu_margin=margin, **kw)
+    _colx_check(case, out, scaling, "e4m3", layout, scale=scale)
+    assert_ws_clean()
+
+
+@pytest.mark.parametrize("scaling", ["delayed", "mxfp8"])
+@pytest.mark.parametrize("variant", ["e5m2", "f16", "bf16_weights_zc", "padded"])
+def test_fwd_colx_variants(scaling, variant):
+    """The single-pass kernel with E5M2 codes, float16 input, bfloat16 zero-centred weights, and
+    (MXFP8) padded scale grids whose padding stays as the caller filled it."""
+    rows, hidden = 512, 3072
+    in_dt = "f16" if variant == "f16" else "bf16"
+    w_dt = "bf16" if variant == "bf16_weights_zc" else "f32"
+    zc = variant == "bf16_weights_zc"
+    fp8 = "e5m2" if variant == "e5m2" else "e4m3"
+    if variant == "padded" and scaling == "delayed":
+        pytest.skip("padded grids are MXFP8's")
+    case = workloads.small_case("rmsnorm", rows, hidden, in_dt, w_dt, seed=31, zero_centered_gamma=zc)
+    assert _colx_planned(rows, hidden, in_dt, scaling, "rowwise_colwise", 0)
+    ref_max = float(np.max(np.abs(oracle_fwd(case, "rmsnorm", in_dt, w_dt, zc)["v"])))
+    kw, scale = _colx_kw(case, scaling, fp8, ref_max)
+    x, g = gpu(case, "x", "gamma")
+    with env(NORMFP8_COLX=1):
+        if variant == "padded":
+            out, call = nf.prepare_fwd(x, g, None, norm="rmsnorm", eps=EPS, layout="rowwise_colwise",
+                                       scales_padded=True, **kw)
+            for k in ("scale_inv", "colwise_scale_inv"):
+                out[k].fill_(SENTINEL)
+            call()
+            torch.cuda.synchronize()
+            for k, (a, c) in (("scale_inv", (rows, hidden // 32)), ("colwise_scale_inv", (hidden, rows // 32))):
+                pad = out[k].clone()
+                pad[:a, :c] = SENTINEL
+                assert bool((pad == SENTINEL).all()), f"{k}: padding written"
+                out[k] = out[k][:a, :c].contiguous()
+        else:
+            out = nf.fwd(x, g, None, norm="rmsnorm", eps=EPS, zero_centered_gamma=zc, layout="rowwise_colwise", **kw)
+    _colx_check(case, out, scaling, fp8, "rowwise_colwise", in_dt, w_dt, zc, scale)
+    assert_ws_clean()
+
+
+def test_fwd_colx_matches_two_pass_statistics():
+    """The single-pass kernel's rsigma (slice partials summed in one fixed order) agrees with the
+    two-pass route's to a few ulps, and both kernels' codes differ only where the oracle allows."""
+    rows, hidden = 1024, 6144
+    case = workloads.small_case("rmsnorm", rows, hidden, "bf16", "f32", seed=77)
+    x, g = gpu(case, "x", "gamma")
+    outs = {}
+    for k in (0, 1):
+        with env(NORMFP8_COLX=k):
+            outs[k] = nf.fwd(x, g, None, norm="rmsnorm", eps=EPS, scaling="mxfp8", layout="rowwise_colwise")
+    a, b = outs[0]["rsigma"].cpu().numpy(), outs[1]["rsigma"].cpu().numpy()
+    assert np.max(np.abs(a - b) / np.abs(a)) < 4 * 2.0 ** -23
+    for k in (0, 1):
+        _colx_check(case, outs[k], "mxfp8", "e4m3", "rowwise_colwise")
+
+
 # ------------------------------------------------------------------------------ determinism
 
 def test_repeat_runs_are_bitwise_identical():
