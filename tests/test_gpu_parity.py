@@ -634,10 +634,11 @@ def test_fwd_split_zero_centered_bf16_weights_and_margin(norm):
 
 # ------------------------------------------------------------------------------ single-pass columnwise
 
-# (rows, hidden, cu_margin): 1 to 24 slices of 512 columns; margins that leave one group of
-# slices walking every band (an odd band count ends the two-band pipeline on its first half)
+# (rows, hidden, cu_margin): 1 to 24 slices of 512 columns; margins that leave one or two groups
+# of slices walking many 128-row super-bands (2 to 18 pipeline steps; step counts of 4k and 4k + 2
+# end the four-band rotation at either of its two exits)
 COLX_SHAPES = [(128, 512, 0), (256, 1536, 0), (384, 4096, 0), (128, 12288, 0), (1024, 2048, 250),
-               (640, 8192, 240), (768, 4096, 0), (1152, 1024, 254)]
+               (640, 8192, 240), (768, 4096, 0), (1152, 1024, 254), (1920, 1024, 252)]
 
 
 def _colx_planned(rows, hidden, in_dt, scaling, layout, margin):
