@@ -112,9 +112,11 @@ int norm_bwd_workspace_size(int64_t rows, int64_t hidden, int in_dtype, int w_dt
 
 /*
  * norm_fwd -- normalise each row of x and store the output, optionally FP8-quantised, in one
- * kernel launch (two when a columnwise layout is requested: the row statistics first, then the
- * codes; both on `stream`). [XLA-Norm] Overview, Description, Signature (NormForwardFFI
- * argument list), I/O Contract.
+ * kernel launch on `stream`. Columnwise layouts take one launch for RMSNorm with 16-bit input,
+ * hidden a multiple of 512 and rows a multiple of 128 (x read once; the workgroups holding a
+ * band of rows exchange their row sums through the workspace), and two otherwise (the row
+ * statistics or rowwise codes first, then the columnwise codes). [XLA-Norm] Overview,
+ * Description, Signature (NormForwardFFI argument list), I/O Contract.
  *
  *   x [rows, hidden] in_dtype; gamma [hidden] w_dtype; beta [hidden] w_dtype (LayerNorm only,
  *   must be NULL for RMSNorm).
@@ -246,7 +248,9 @@ int norm_bwd_launch_shape(int64_t rows, int64_t hidden, int in_dtype, int w_dtyp
  * NORMFP8_DELAYED_TRANSPOSE (0: statistics + tile route for delayed scaling with both
  * outputs), NORMFP8_TRANSPOSE_TC / NORMFP8_TRANSPOSE_RL (byte-transpose tile shape),
  * NORMFP8_ROW_OCC (cap on row-kernel workgroups per CU), NORMFP8_ROW_BALANCE (0: plain
- * occupancy grid), NORMFP8_BAND_CLASSES (1: one ticket class). Unknown names give
+ * occupancy grid), NORMFP8_BAND_CLASSES (1: one ticket class), NORMFP8_SPLIT (0: no split
+ * kernel for long rows; 1: split kernel for every row it covers), NORMFP8_COLX (0: two-pass
+ * routes instead of the single-pass columnwise kernel). Unknown names give
  * NORM_ERR_INVALID_ARG. Not for the hot path of an application: a change affects every later
  * call in the process.
  */
