@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kColxThreads) void fwd_colx_kernel(FwdColxParams cp
   const FwdRowParams &p = cp.f;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: role tests branch on it)
   const int q = wave >> 1;        // sub-tile of the slice
   const int wh = wave & 1;        // 32-row half of the band
   const int rg = lane >> 4;       // row group within the wave
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kColxThreads) void fwd_colx_kernel(FwdColxParams cp
     }
   };
 
-  // ---- the slice's 64 row sums of squares of a loaded band, into rpart (ends with a barrier)
+  // ---- the slice's 64 row sums of squares of a loaded band, into rpart (read after a barrier)
   auto row_sums = [&](Tile &t) {
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
@@ -195,7 +195,6 @@ __global__ __launch_bounds__(kColxThreads) void fwd_colx_kernel(FwdColxParams cp
     }
 #pragma unroll
     for (int k = 0; k < KR; ++k) opaque<IN>(t[k]);
-    __syncthreads();
   };
   // waves 2-3: band j's partials, published
   auto publish = [&](int64_t j) {
@@ -387,22 +386,23 @@ __global__ __launch_bounds__(kColxThreads) void fwd_colx_kernel(FwdColxParams cp
   };
 
   // step j: cur holds band j (its partials published two steps ago), sm holds band j + 2 (loaded
-  // a step ago: its sums are published now), ld receives band j + 3
+  // a step ago), ld receives band j + 3. Waves 0-1 poll band j while the others' loads go out; then
+  // band j's codes and band j + 2's row sums; then waves 2-3 publish those sums and waves 4-7 write
+  // band j's outputs. The row sums run on every step, also past the group's last band (on a tile
+  // that was not loaded; nothing is published): every tile's loads are then waited for there, two
+  // steps before its codes, on every path, so the compiler puts no wait for loads in flight into
+  // the codes.
   auto step = [&](Tile &cur, Tile &sm, Tile &ld, int64_t j) {
     const bool do_ld = j + 3 < nb, do_sm = j + 2 < nb;
 #pragma unroll
     for (int k = 0; k < KR; ++k) fresh<IN>(ld[k]);
-    if (wave < kPollWaves) {
-      poll(j);
-    } else if (do_ld) {
-      load_tile(ld, j + 3);
-    }
+    if (wave < kPollWaves) poll(j);
+    else if (do_ld) load_tile(ld, j + 3);
     __syncthreads();
     if (wave < kPollWaves && do_ld) load_tile(ld, j + 3);
     codes(cur, j);
+    row_sums(sm);
     __syncthreads();
-    if (do_sm) row_sums(sm);
-    else __syncthreads();
     if (do_sm) publish(j + 2);
     if (wave >= kStoreWave0) store(j);
   };
@@ -415,10 +415,13 @@ __global__ __launch_bounds__(kColxThreads) void fwd_colx_kernel(FwdColxParams cp
     load_tile(T1, 1);
     if (nb > 2) load_tile(T2, 2);
     row_sums(T0);
+    __syncthreads();
     publish(0);
     __syncthreads();
     row_sums(T1);
+    __syncthreads();
     publish(1);
+    __syncthreads();  // (the first step's sums rewrite rpart)
   }
   for (int64_t j = 0; j < nb; j += 4) {
     step(T0, T2, T3, j);
