@@ -667,7 +667,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
   if (pl.colx) {
     // (the two-pass routes serve what this kernel cannot: scale grids not 16 / 4-byte aligned, or
     // a CU margin that leaves fewer resident workgroups than one band's slices)
-    const void *fn = fwd_colx_kernel_ptr(in_dtype, pl.mode);
+    const void *fn = fwd_colx_kernel_ptr(in_dtype, out_dtype, pl.mode);
     int occ = 1;
     if (fn) {
       rc = occupancy(fn, kColxThreads, &occ);

@@ -214,16 +214,20 @@ __device__ __forceinline__ uint2 fp8_pack8(const float (&u)[8], int fmt) {
   float c[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(u[i], -m, m);
+  // (the first conversion of each word keeps its destination's high half, which the second
+  // overwrites: passing the first input's own bits there lets it convert in place, with no
+  // copy of a zero into the destination)
   int w0, w1;
+  const int k0 = (int)__float_as_uint(c[0]), k4 = (int)__float_as_uint(c[4]);
   if (fmt == DT_E4M3) {
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], k0, false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w0, true);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], k4, false);
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], w1, true);
   } else {
-    w0 = __builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], k0, false);
     w0 = __builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], w0, true);
-    w1 = __builtin_amdgcn_cvt_pk_bf8_f32(c[4], c[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_bf8_f32(c[4], c[5], k4, false);
     w1 = __builtin_amdgcn_cvt_pk_bf8_f32(c[6], c[7], w1, true);
   }
   return make_uint2((uint32_t)w0, (uint32_t)w1);

@@ -87,7 +87,7 @@ template <class T> __device__ __forceinline__ void fresh(Strip<T> &s) {
 
 }  // namespace
 
-template <class IN, int MODE>
+template <class IN, int MODE, int FMT>
 __global__ __launch_bounds__(kColxThreads) void fwd_colx_kernel(FwdColxParams cp) {
   static_assert(MODE == MODE_DELAYED || MODE == MODE_MX, "columnwise output is FP8");
   static_assert(kColxThreads == 512 && kColxRows == kXS && kColxCols == 512, "8 waves: 2 per 64 x 128 sub-tile");
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kColxThreads) void fwd_colx_kernel(FwdColxParams cp
   const int64_t H = p.hidden;
   const int64_t N = p.rows;
   const int S = cp.S;
-  const int fmt = p.out_dtype;
+  constexpr int fmt = FMT;  // (a compile-time format: one conversion path, no selects)
   constexpr int TW = kColxCols;
   constexpr int kPollWaves = 2, kPubWave0 = 2, kStoreWave0 = 4;
   constexpr int ST = kColxThreads - 64 * kStoreWave0;  // storing threads (256)
@@ -461,20 +461,29 @@ __global__ __launch_bounds__(kColxThreads) void fwd_colx_kernel(FwdColxParams cp
   }
 }
 
-template <class IN>
+template <class IN, int FMT>
 static const void *pick_colx_mode(int mode) {
   switch (mode) {
-    case MODE_DELAYED: return (const void *)fwd_colx_kernel<IN, MODE_DELAYED>;
-    case MODE_MX: return (const void *)fwd_colx_kernel<IN, MODE_MX>;
+    case MODE_DELAYED: return (const void *)fwd_colx_kernel<IN, MODE_DELAYED, FMT>;
+    case MODE_MX: return (const void *)fwd_colx_kernel<IN, MODE_MX, FMT>;
     default: return nullptr;
   }
 }
 
-const void *fwd_colx_kernel_ptr(int in_dtype, int mode) {
+template <class IN>
+static const void *pick_colx_fmt(int out_dtype, int mode) {
+  switch (out_dtype) {
+    case DT_E4M3: return pick_colx_mode<IN, DT_E4M3>(mode);
+    case DT_E5M2: return pick_colx_mode<IN, DT_E5M2>(mode);
+    default: return nullptr;
+  }
+}
+
+const void *fwd_colx_kernel_ptr(int in_dtype, int out_dtype, int mode) {
   switch (in_dtype) {
-    // (float32 input: two bands would fill the registers; the two-pass routes serve it)
-    case DT_BF16: return pick_colx_mode<BF16>(mode);
-    case DT_F16: return pick_colx_mode<F16>(mode);
+    // (float32 input: four bands would fill the registers; the two-pass routes serve it)
+    case DT_BF16: return pick_colx_fmt<BF16>(out_dtype, mode);
+    case DT_F16: return pick_colx_fmt<F16>(out_dtype, mode);
     default: return nullptr;
   }
 }

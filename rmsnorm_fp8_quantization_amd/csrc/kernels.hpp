@@ -91,7 +91,7 @@ constexpr int kColThreads = 4 * kColTileRows;  // 16 rows per wave
 const void *fwd_row_kernel_ptr(int norm, int in_dtype, int mode, int cfg);
 const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg);
 const void *fwd_split_kernel_ptr(int norm, int in_dtype);
-const void *fwd_colx_kernel_ptr(int in_dtype, int mode);  // RMSNorm only
+const void *fwd_colx_kernel_ptr(int in_dtype, int out_dtype, int mode);  // RMSNorm only
 const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor);
 // tiles of 32 * rows_per_lane rows x 256 columns (rows_per_lane 4 or 8), or of 512 rows x 128
 // columns (tile_cols 128, rows_per_lane 8)
