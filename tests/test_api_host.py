@@ -244,3 +244,44 @@ def test_scales_padded_layout_validation():
     assert fwd_ws(100, 1000, layout=L.NORM_Q_ROWWISE | pad)[0] == L.NORM_ERR_INVALID_ARG
     # the modifier alone is not a layout
     assert fwd_ws(100, 1000, layout=pad, **mx)[0] == L.NORM_ERR_INVALID_ARG
+
+
+def _rup(a, m):
+    return (a + m - 1) // m * m
+
+
+@pytest.mark.parametrize("scaling", ["delayed", "mxfp8"])
+def test_single_pass_columnwise_planning(scaling):
+    """The planner sends RMSNorm with a transposed columnwise FP8 output on 16-bit input, hidden a
+    multiple of 512 and rows a multiple of 128 to the single-pass kernel: its workspace is the
+    header, the tagged row sums [rows / 64, S, 64] (S = hidden / 512) and the statistics block of
+    a columnwise request. Everything else keeps the two-pass workspace (no row sums)."""
+    sc = {"delayed": L.NORM_SCALING_DELAYED_TENSOR, "mxfp8": L.NORM_SCALING_MXFP8_1D32}[scaling]
+    hdr = L.NORM_WS_HEADER_BYTES
+
+    def q(rows, hidden, **kw):
+        kw.setdefault("layout", L.NORM_Q_ROWWISE_COLWISE)
+        rc, n = fwd_ws(rows, hidden, out=L.NORM_FP8_E4M3, scaling=sc, **kw)
+        assert rc == L.NORM_OK
+        return n
+
+    def single(rows, hidden):
+        return hdr + _rup(rows * (hidden // 512) * 8, 256) + _rup(rows * 4, 256)
+
+    for rows, hidden in ((16384, 12288), (32768, 8192), (128, 512), (1920, 1024)):
+        assert q(rows, hidden) == single(rows, hidden), (rows, hidden)
+        assert q(rows, hidden, layout=L.NORM_Q_COLWISE) == single(rows, hidden)
+        assert q(rows, hidden, in_dt=L.NORM_F16) == single(rows, hidden)
+    for rows, hidden, kw in ((16384, 12288, dict(in_dt=L.NORM_F32)),        # float32 input
+                             (16383, 12288, {}), (16384, 12000, {}),        # shapes it does not tile
+                             (16384, 12288, dict(norm=L.NORM_LAYERNORM)),  # LayerNorm
+                             (16384, 12288, dict(layout=L.NORM_Q_COLWISE | L.NORM_Q_COLWISE_ROWMAJOR))):
+        # (two-pass workspaces: the statistics block, plus the header for delayed scaling)
+        assert q(rows, hidden, **kw) <= hdr + _rup(rows * 8, 256), (rows, hidden, kw)
+    prev = ctypes.c_int(0)
+    assert L.status("norm_tuning_set", b"NORMFP8_COLX", 0, ctypes.byref(prev)) == L.NORM_OK
+    try:
+        assert q(16384, 12288) != single(16384, 12288)
+    finally:
+        L.status("norm_tuning_set", b"NORMFP8_COLX", prev.value, None)
+    assert q(16384, 12288) == single(16384, 12288)

@@ -754,13 +754,23 @@ def test_fwd_colx_matches_two_pass_statistics():
 
 def test_repeat_runs_are_bitwise_identical():
     """Repeated calls give the same bytes: the band split (forced: its cross-workgroup exchange
-    of row partials through tagged words and tickets), the columnwise tile path, the single-pass
-    columnwise band kernel and the backward's fixed-order partial reduction."""
+    of row partials through tagged words and tickets), the split kernel, the columnwise tile path,
+    the single-pass columnwise band kernel, the single-pass RMSNorm columnwise kernel (row sums
+    exchanged between 512-column slices; MXFP8 and delayed) and the backward's fixed-order partial
+    reduction."""
     case = workloads.small_case("layernorm", 500, 20480, "bf16", "f32", seed=8)
     dy, x, g, b = gpu(case, "dy", "x", "gamma", "beta")
     xs, dys, gs = x[:, :16384].contiguous(), dy[:, :16384].contiguous(), g[:16384].contiguous()
+    xr, gr = x[:384, :6144].contiguous(), g[:6144].contiguous()   # 3 super-bands x 12 slices
+    st = torch.tensor([16.0], device="cuda")
     outs = []
     for _ in range(3):
+        with env(NORMFP8_COLX=1):
+            fm = nf.fwd(xr, gr, None, norm="rmsnorm", scaling="mxfp8", layout="rowwise_colwise")
+            fd = nf.fwd(xr, gr, None, norm="rmsnorm", scaling="delayed", scale=st,
+                        amax=torch.zeros(1, device="cuda"), layout="rowwise_colwise")
+        outs_x = [fm["y"], fm["y_colwise"], fm["scale_inv"], fm["colwise_scale_inv"], fm["rsigma"],
+                  fd["y"], fd["y_colwise"], fd["amax"], fd["rsigma"]]
         with env(NORMFP8_FORCE_BAND=1, NORMFP8_SPLIT=0):
             f = nf.fwd(x, g, b, norm="layernorm")                  # band split (20480 columns)
         with env(NORMFP8_SPLIT=1):
@@ -772,7 +782,7 @@ def test_repeat_runs_are_bitwise_identical():
         outs.append([t.clone() for t in (f["y"], f["mu"], f["rsigma"], fs["y"], fs["mu"], fs["rsigma"],
                                           fb["y"], fb["y_colwise"], fb["rsigma"],
                                           fc["y"], fc["y_colwise"], fc["colwise_scale_inv"],
-                                          d["dx"], d["dgamma"], d["dbeta"])])
+                                          d["dx"], d["dgamma"], d["dbeta"], *outs_x)])
     for o in outs[1:]:
         for a, b_ in zip(outs[0], o):
             assert torch.equal(a.view(torch.uint8), b_.view(torch.uint8))
