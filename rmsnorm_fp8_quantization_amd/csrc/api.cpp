@@ -887,6 +887,20 @@ static int bwd_common(void *stream, bool with_add, const void *dy, const void *x
     return ok();
   }
 
+  if (rows == 0) {
+    // nothing to read (the row-indexed pointers may be NULL): the finalize kernel over zero
+    // partial rows writes zero gradients
+    FinalizeParams fp{};
+    fp.part = reinterpret_cast<const float *>(static_cast<char *>(workspace) + kWsHeaderBytes);
+    fp.dgamma = dgamma;
+    fp.dbeta = ln ? dbeta : nullptr;
+    fp.hidden = hidden;
+    fp.G = 0;
+    fp.w_dtype = w_dtype;
+    rc = launch(bwd_finalize_kernel_ptr(), dim3((unsigned)cdiv(hidden, 32), ln ? 2 : 1), dim3(256), &fp, st);
+    if (rc) return rc;
+    return ok();
+  }
   const void *fn = bwd_kernel_ptr(norm_type, in_dtype, with_add, pl.cfg);
   if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no backward kernel for this combination");
   const BwdShape &sh = kBwdShapes[pl.cfg];
@@ -909,8 +923,6 @@ static int bwd_common(void *stream, bool with_add, const void *dy, const void *x
   p.w_dtype = w_dtype;
   p.zero_centered = zero_centered_gamma ? 1 : 0;
   p.G = (int)G;
-  // rows == 0: the row kernel has no rows to visit but still writes zero partials, so the
-  // finalize step returns zero gradients
   rc = launch(fn, dim3((unsigned)G), dim3(sh.threads()), &p, st);
   if (rc) return rc;
 

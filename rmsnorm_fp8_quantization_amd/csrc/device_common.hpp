@@ -428,7 +428,8 @@ __device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
 // the tag of the launch that observed `epoch` at its start (never 0)
 __device__ __forceinline__ uint32_t epoch_tag(uint32_t epoch) { return epoch == 0xffffffffu ? 1u : epoch + 1u; }
 
-// Value of a tagged word once it carries `tag` (polls; time-limited like spin_until_ge).
+// Value of a tagged word once it carries `tag`. Polls; after kSpinLimitTicks it sets bit 0 of
+// *err and returns what it last read.
 __device__ __forceinline__ float wait_tagged(const uint64_t *p, uint32_t tag, uint32_t *err) {
   uint64_t v = ld_dev64(p);
   if ((uint32_t)(v >> 32) == tag) return __uint_as_float((uint32_t)v);

@@ -581,6 +581,34 @@ def test_bwd_zero_rows_gives_zero_gradients():
     assert torch.all(out["dgamma"] == 0) and torch.all(out["dbeta"] == 0)
 
 
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm", "rmsnorm_add"])
+def test_bwd_zero_rows_with_null_row_pointers(kind):
+    """rows == 0 with every row-indexed pointer NULL (allowed by the boundary): zero gradients,
+    nothing read."""
+    import ctypes
+    from rmsnorm_fp8_quantization_amd import _lib as L, ops
+    norm = "rmsnorm" if kind.startswith("rms") else "layernorm"
+    add = kind == "rmsnorm_add"
+    hidden = 4096
+    dev = torch.device("cuda")
+    g = torch.randn(hidden, device=dev)
+    dg = torch.full((hidden,), 7.0, device=dev)
+    db = torch.full((hidden,), 7.0, device=dev) if norm == "layernorm" else None
+    ws = ops.workspace(ops.bwd_workspace_size(0, hidden, torch.bfloat16, torch.float32, norm, add), dev)
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if add:
+        L.call("norm_bwd_add", stream, None, None, None, None, p(g), None, p(dg), p(ws), ws.numel(), 0, hidden,
+               L.NORM_BF16, L.NORM_F32, 0, 0)
+    else:
+        L.call("norm_bwd", stream, None, None, None, None, p(g), None, p(dg), p(db), p(ws), ws.numel(), 0, hidden,
+               L.NORM_BF16, L.NORM_F32, L.NORM_LAYERNORM if norm == "layernorm" else L.NORM_RMSNORM, 0, 0)
+    torch.cuda.synchronize()
+    assert torch.all(dg == 0)
+    if db is not None:
+        assert torch.all(db == 0)
+
+
 def test_fwd_then_bwd_end_to_end():
     """GPU statistics feeding the GPU backward, against the oracle with its own statistics."""
     case = workloads.small_case("layernorm", 128, 4096, "bf16", "f32", seed=77)
