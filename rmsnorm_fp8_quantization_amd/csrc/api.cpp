@@ -235,8 +235,10 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     // 128 KB of LDS weights (16 waves per CU, where the weights in registers left room for 8:
     // bf16 16384 x 12288 192 -> 163 us); RMSNorm rows of 8193..16384 elements run on 16 waves
     // with their few weights in registers, two workgroups per CU
-    const int pref_ln[] = {ROW_W1_K1, ROW_W1_K2, ROW_W1_K4, ROW_W2T2_K4, ROW_W4T4_K4, ROW_W8T2_K4, ROW_W16_K8};
-    const int pref_rms[] = {ROW_W1_K1, ROW_W1_K2, ROW_W1_K4, ROW_W2T2_K4, ROW_W4_K4, ROW_W16_K2, ROW_W16_K8};
+    const int pref_ln[] = {ROW_W1_K1,   ROW_W1_K2,   ROW_W1_K4,  ROW_W2T2_K4,
+                           ROW_W4T4_K4, ROW_W8T2_K4, ROW_W16_K4, ROW_W16_K8};
+    const int pref_rms[] = {ROW_W1_K1, ROW_W1_K2,  ROW_W1_K4,  ROW_W2T2_K4,
+                            ROW_W4_K4, ROW_W16_K2, ROW_W16_K4, ROW_W16_K8};
     for (int c : norm_type == NORM_LAYERNORM ? pref_ln : pref_rms)
       if (kRowShapes[c].cover() >= hidden) {
         row_cfg = c;

@@ -415,6 +415,10 @@ static const void *pick_cfg(int cfg) {
     // weights in LDS whatever their size (LayerNorm: 128 KB for 16384 elements, one workgroup
     // of 16 waves per CU)
     case ROW_W8T2_K4: return (const void *)fwd_row_kernel<NORM, IN, MODE, 8, 2, 4, 1>;
+    // RMSNorm: gamma in registers (32 per lane, loaded once per persistent workgroup);
+    // LayerNorm's gamma and beta would need 64 and spill, so they are read per strip
+    case ROW_W16_K4:
+      return (const void *)fwd_row_kernel<NORM, IN, MODE, 16, 1, 4, NORM == NT_LAYERNORM ? 2 : 0>;
     default: return nullptr;
   }
 #undef NF8_ROW

@@ -99,7 +99,8 @@ def test_fwd_plain_other_out_dtype_and_bf16_weights(out_dt):
     checks.check_hp(bits(out["y"]), ref["v"], out_dt, terms=ln_terms(case, ref, "layernorm", "bf16"))
 
 
-ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096, 65536, 8192, 16384, 16384]   # per row layout
+ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096, 65536, 8192, 16384, 16384,
+             32768]   # per row layout
 BWD_COVER = [1024, 2048, 4096, 8192, 16384, 4096, 8192, 8192, 1024, 2048, 4096, 12288]
 
 
@@ -118,8 +119,9 @@ def test_fwd_every_row_layout(cfg, norm):
     checks.check_hp(bits(out["y"]), ref["v"], "bf16", terms=ln_terms(case, ref, norm))
 
 
-# rows longer than 16384 elements: the 16-wave layout whose weights are read from the caches a
-# strip ahead of their use; rows of 8193..16384 elements: RMSNorm FP8 epilogues on 8 waves x
+# rows of 32769..65536 elements: 16 waves x 8 strips, weights read from the caches a strip ahead
+# of their use; rows of 16385..32768: 16 waves x 4 strips (RMSNorm's gamma in registers,
+# LayerNorm's gamma and beta from the caches); rows of 8193..16384 elements: RMSNorm FP8 epilogues on 8 waves x
 # 4 strips, its plain outputs on 16 waves x 2 strips, LayerNorm on two 8-wave rows per
 # workgroup sharing the LDS weights; RMSNorm FP8 rowwise epilogues at 2049..4096 elements on
 # 4 waves x 2 rows x 2 strips (any weight dtype, zero-centred gamma, every rowwise epilogue)
@@ -127,6 +129,8 @@ def test_fwd_every_row_layout(cfg, norm):
 @pytest.mark.parametrize("mode", ["none", "delayed", "mxfp8"])
 @pytest.mark.parametrize("norm,hidden,zc", [("layernorm", 65536, False), ("rmsnorm", 65536, True),
                                             ("layernorm", 40000, True), ("rmsnorm", 20488, False),
+                                            ("layernorm", 32768, False), ("rmsnorm", 32760, True),
+                                            ("layernorm", 16392, True),
                                             ("rmsnorm", 12288, True), ("rmsnorm", 10232, False),
                                             ("rmsnorm", 16384, False), ("layernorm", 12288, True),
                                             ("layernorm", 10232, False), ("rmsnorm", 4096, True),
