@@ -70,6 +70,51 @@ template <> __device__ __forceinline__ void strip_to_f32<F16>(const Strip<F16> &
   o[6] = f16_lo(s.v[0].w); o[7] = f16_hi(s.v[0].w);
 }
 
+// Sum and sum of squares of a strip's 8 values. 16-bit inputs: one packed dot product per pair
+// of values (with (1, 1), or with the pair itself), accumulated in binary32 -- the products of
+// 16-bit values are exact in binary32 -- so a strip costs 4 instructions and no conversions.
+typedef __bf16 nf8_bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 nf8_f16x2 __attribute__((ext_vector_type(2)));
+template <class T> __device__ __forceinline__ float strip_sum(const Strip<T> &s);
+template <> __device__ __forceinline__ float strip_sum<F32>(const Strip<F32> &s) {
+  float o[8];
+  strip_to_f32<F32>(s, o);
+  return ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
+}
+template <> __device__ __forceinline__ float strip_sum<BF16>(const Strip<BF16> &s) {
+  const uint32_t w[4] = {s.v[0].x, s.v[0].y, s.v[0].z, s.v[0].w};
+  const nf8_bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float a = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(nf8_bf16x2, w[d]), one, a, false);
+  return a;
+}
+template <> __device__ __forceinline__ float strip_sum<F16>(const Strip<F16> &s) {
+  const uint32_t w[4] = {s.v[0].x, s.v[0].y, s.v[0].z, s.v[0].w};
+  const nf8_f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  float a = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) a = __builtin_amdgcn_fdot2(__builtin_bit_cast(nf8_f16x2, w[d]), one, a, false);
+  return a;
+}
+template <class T> __device__ __forceinline__ float strip_sumsq(const Strip<T> &s);
+template <> __device__ __forceinline__ float strip_sumsq<BF16>(const Strip<BF16> &s) {
+  const uint32_t w[4] = {s.v[0].x, s.v[0].y, s.v[0].z, s.v[0].w};
+  float a = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(nf8_bf16x2, w[d]), __builtin_bit_cast(nf8_bf16x2, w[d]), a, false);
+  return a;
+}
+template <> __device__ __forceinline__ float strip_sumsq<F16>(const Strip<F16> &s) {
+  const uint32_t w[4] = {s.v[0].x, s.v[0].y, s.v[0].z, s.v[0].w};
+  float a = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    a = __builtin_amdgcn_fdot2(__builtin_bit_cast(nf8_f16x2, w[d]), __builtin_bit_cast(nf8_f16x2, w[d]), a, false);
+  return a;
+}
+
 // Register-pressure barrier: makes the compiler treat a strip's packed registers as changed,
 // so values converted from them before this point are not kept alive to be reused after it
 // (emits no instruction).

@@ -77,29 +77,6 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// Sum of squares of a strip's 8 values. 16-bit inputs: one dot product of each packed pair with
-// itself, accumulated in binary32 (a product of two 16-bit values is exact in binary32), so the 8
-// squares cost 4 instructions and no conversions.
-template <class T> __device__ __forceinline__ float strip_sumsq(const Strip<T> &s);
-template <> __device__ __forceinline__ float strip_sumsq<BF16>(const Strip<BF16> &s) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const uint32_t w[4] = {s.v[0].x, s.v[0].y, s.v[0].z, s.v[0].w};
-  float a = 0.0f;
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[d]), __builtin_bit_cast(bf16x2, w[d]), a, false);
-  return a;
-}
-template <> __device__ __forceinline__ float strip_sumsq<F16>(const Strip<F16> &s) {
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  const uint32_t w[4] = {s.v[0].x, s.v[0].y, s.v[0].z, s.v[0].w};
-  float a = 0.0f;
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-    a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[d]), __builtin_bit_cast(f16x2, w[d]), a, false);
-  return a;
-}
-
 // a new definition of a strip's registers without an instruction: the value a tile held before
 // is dead from here on, though the compiler cannot see that every path reloads the tile
 template <class T> __device__ __forceinline__ void fresh(Strip<T> &s) {

@@ -210,12 +210,7 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
       {
         float sa = 0.0f;
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-          float xv[8];
-          strip_to_f32<IN>(cur[k], xv);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sa += xv[i];  // (strips past the end are zero)
-        }
+        for (int k = 0; k < KC; ++k) sa += strip_sum<IN>(cur[k]);  // (strips past the end are zero)
         // (through readfirstlane: the shift is rounded once and every use sees that value; a
         // product left in a register would be fused into each x - K as an fma, putting the
         // deviations in a frame of the unrounded product)
