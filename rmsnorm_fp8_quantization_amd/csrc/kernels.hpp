@@ -22,7 +22,10 @@ enum RowCfg : int {
   ROW_W4T4_K4,  // 4 waves per row, 4 rows per workgroup: the rows share the LDS weights
   ROW_W16_K2,   // 16 waves per row, 2 strips per lane (RMSNorm rows of 8193..16384)
   ROW_W8T2_K4,  // 8 waves per row, 2 rows per workgroup sharing 128 KB of LDS weights
-  ROW_W16_K4,   // 16 waves per row, 4 strips per lane, weights in registers (rows of 16385..32768)
+  ROW_W16_K4,   // 16 waves per row, 4 strips per lane (rows of 16385..32768)
+  ROW_W8_K8,    // 8 waves per row, 8 strips per lane, gamma and beta in registers (LayerNorm rows of
+                // 16385..32768, 16-bit input, no FP8 epilogue; instantiated for 16-bit plain and
+                // statistics-only passes only)
   ROW_NCFG
 };
 struct RowShape {
@@ -32,7 +35,7 @@ struct RowShape {
 };
 constexpr RowShape kRowShapes[ROW_NCFG] = {{1, 4, 1}, {1, 4, 2}, {1, 4, 4}, {1, 4, 8}, {4, 1, 2}, {4, 1, 4},
                                            {8, 1, 4}, {2, 2, 4}, {8, 1, 1}, {4, 2, 2}, {16, 1, 8},
-                                           {4, 4, 4}, {16, 1, 2}, {8, 2, 4}, {16, 1, 4}};
+                                           {4, 4, 4}, {16, 1, 2}, {8, 2, 4}, {16, 1, 4}, {8, 1, 8}};
 
 // ---- forward band kernel: 4 waves, RW rows per wave, KC strips per lane
 enum BandCfg : int { BAND_R8_K1 = 0, BAND_R8_K2, BAND_R4_K2, BAND_R1_K4, BAND_R2_K8, BAND_NCFG };
