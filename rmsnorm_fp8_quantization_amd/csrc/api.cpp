@@ -66,7 +66,8 @@ constexpr int kKnobUnset = INT_MIN;
 const char *const kKnobNames[] = {"NORMFP8_FORCE_BAND",       "NORMFP8_ROW_CFG",      "NORMFP8_COL_KERNEL",
                                   "NORMFP8_DELAYED_TRANSPOSE", "NORMFP8_BAND_CFG",     "NORMFP8_BWD_CFG",
                                   "NORMFP8_ROW_OCC",           "NORMFP8_ROW_BALANCE",  "NORMFP8_TRANSPOSE_TC",
-                                  "NORMFP8_TRANSPOSE_RL",      "NORMFP8_BAND_CLASSES", "NORMFP8_SPLIT", "NORMFP8_COLX"};
+                                  "NORMFP8_TRANSPOSE_RL",      "NORMFP8_BAND_CLASSES", "NORMFP8_SPLIT", "NORMFP8_COLX",
+                                  "NORMFP8_SPLIT_SHAPE"};
 enum Knob : int {
   K_FORCE_BAND = 0,
   K_ROW_CFG,
@@ -81,6 +82,7 @@ enum Knob : int {
   K_BAND_CLASSES,
   K_SPLIT,
   K_COLX,
+  K_SPLIT_SHAPE,
   K_NKNOBS
 };
 static_assert(sizeof(kKnobNames) / sizeof(kKnobNames[0]) == K_NKNOBS, "knob table");
@@ -172,6 +174,7 @@ struct FwdPlan {
   bool tr = false;    // delayed scaling, rowwise + columnwise: row kernel, then a byte transpose
   bool gen = false;   // general kernels: hidden not a multiple of 8 (or, at launch, unaligned tensors)
   bool split = false; // long rows, no FP8 epilogue: the split kernel (S slices per row, weights in LDS)
+  int split_shape = 0; // the split kernel's shape (kSplitShapes)
   bool colx = false;  // RMSNorm FP8 with a columnwise output: the single-pass band-exchange kernel
 };
 
@@ -180,6 +183,11 @@ struct FwdPlan {
 // the band kernel); up to 65536 the one-workgroup-per-row layout is faster (LayerNorm
 // 1024 x 65536: 68 against 72 us; RMSNorm 52 against 63 us)
 constexpr int64_t kSplitMinHidden = 65536 + 8;
+// LayerNorm with a 16-bit input: the 8-wave split shape (gamma in registers, beta in LDS) from
+// rows of 40961 elements on (bf16, one box: 1536 x 49152 78 against 81-85 us in the row layout,
+// 1024 x 65536 65 against 67-74, 682 x 98304 67 against 77 for the 16-wave shape, 512 x 131072
+// 69 against 85)
+constexpr int64_t kSplitMinHiddenLn16 = 40960 + 1;
 
 int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
              int scaling, int qlayout, int cu_margin, FwdPlan *pl) {
@@ -312,13 +320,23 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   }
 
   // long rows without an FP8 epilogue: the split kernel (NORMFP8_SPLIT=0 keeps the row / band
-  // layouts, =1 takes the split kernel for any row it covers)
+  // layouts, =1 takes the split kernel for any row it covers; NORMFP8_SPLIT_SHAPE=0 / 1 picks its
+  // shape)
   {
     const int force = knob(K_SPLIT, -1);
-    const int64_t S = cdiv(hidden, kSplitCols);
+    // shape 1 (8 waves x 8 strips, gamma in registers) takes 16-bit input only; by default it
+    // serves LayerNorm, RMSNorm keeps the 16-wave shape (its weights fit LDS whole)
+    const bool in16 = in_dtype != DT_F32;
+    const int shape_ov = knob(K_SPLIT_SHAPE, -1);
+    int shape = norm_type == NORM_LAYERNORM && in16 ? 1 : 0;
+    if (shape_ov == 0) shape = 0;
+    else if (shape_ov == 1 && in16) shape = 1;
+    const int64_t min_hidden = shape == 1 ? kSplitMinHiddenLn16 : kSplitMinHidden;
+    const int64_t S = cdiv(hidden, kSplitShapes[shape].cols());
     const bool fits = pl->mode == MODE_PLAIN && !pl->colwise && !pl->gen && !force_band && S <= kSplitMaxSlices;
-    if (fits && (force == 1 || (force < 0 && hidden >= kSplitMinHidden))) {
+    if (fits && (force == 1 || (force < 0 && hidden >= min_hidden))) {
       pl->split = true;
+      pl->split_shape = shape;
       pl->band = pl->col = false;
       pl->S = (int)S;
     }
@@ -651,10 +669,11 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     return ok();
   }
   if (pl.split) {
-    const void *fn = fwd_split_kernel_ptr(norm_type, in_dtype);
+    const void *fn = fwd_split_kernel_ptr(norm_type, in_dtype, pl.split_shape);
     if (!fn) return fail(NORM_ERR_UNSUPPORTED, "no split kernel for this combination");
+    const int split_threads = kSplitShapes[pl.split_shape].threads;
     int occ = 1;
-    rc = occupancy(fn, kSplitThreads, &occ);
+    rc = occupancy(fn, split_threads, &occ);
     if (rc) return rc;
     int64_t cap = (int64_t)(dev.cus - cu_margin) * occ;
     if (cap > kMaxGrid) cap = kMaxGrid;
@@ -667,7 +686,7 @@ int norm_fwd(void *stream, const void *x, const void *gamma, const void *beta, c
     sp.f = f;
     sp.partials = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + pl.partial_off);
     sp.S = pl.S;
-    rc = launch(fn, dim3((unsigned)(groups * pl.S)), dim3(kSplitThreads), &sp, st);
+    rc = launch(fn, dim3((unsigned)(groups * pl.S)), dim3(split_threads), &sp, st);
     if (rc) return rc;
     return ok();
   }

@@ -7,12 +7,14 @@
 // CTAs that combine their partial statistics through a workspace. [XLA-Norm] I/O Contract: the
 // forward's outputs y, mu (LayerNorm) and rsigma.
 //
-// A row of H elements is cut into S = ceil(H / 16384) slices. A workgroup of 16 waves owns one
-// slice of every row of its row group: it stages the slice's gamma / beta (float32, 1 + gamma
-// when zero-centred) in LDS once -- 128 KB for LayerNorm -- and then walks its rows, so no
-// weight is read again from the caches per row (a 65536-element row re-read 512 KB of weights
-// per row through the L2 in the one-workgroup-per-row layout). Lane t holds two 16-byte strips
-// of the slice: columns 8 (t + 1024 k), k < 2.
+// A row of H elements is cut into S = ceil(H / W) slices. A workgroup owns one slice of every row
+// of its row group and loads the slice's gamma / beta (float32, 1 + gamma when zero-centred)
+// once, then walks its rows, so no weight is read again from the caches per row (a 65536-element
+// row re-read 512 KB of weights per row through the L2 in the one-workgroup-per-row layout).
+// Lane t holds the strips of columns 8 (t + NT k), k < KC. Two shapes: 16 waves x 2 strips
+// (W = 16384) with both weight arrays in LDS (128 KB for LayerNorm) and four rows in flight; and,
+// for 16-bit input, 8 waves x 8 strips (W = 32768) with gamma in registers (64 per lane), beta in
+// LDS (128 KB) and three rows in flight.
 //
 // Per row: every wave reduces its 1024 elements (LayerNorm: deviations from the wave's plain
 // mean estimate, so that a large common part of the row costs no precision), the 16 wave
@@ -21,7 +23,9 @@
 // words of the row and merges them in slice order, so all S workgroups obtain identical
 // statistics. Four rows are in flight: row j + 3 is loading and row j + 2 publishes its partial
 // while row j is normalised with its partners' words, which were published two rows earlier and
-// loaded one row earlier, so the exchange overlaps the loads of the next rows.
+// loaded one row earlier, so the exchange overlaps the loads of the next rows. With three rows
+// in flight (the 8-wave shape, whose registers hold gamma) row j + 2 loads and row j + 1
+// publishes while row j is normalised: each stage has one row's time to land.
 //
 // Group membership comes from tickets taken at start (group = ticket / S, slice = ticket % S):
 // every ticket is held by a running workgroup, so a workgroup only waits on workgroups that are
@@ -32,11 +36,14 @@
 
 namespace nf8 {
 
-template <int NORM, class IN>
-__global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(FwdSplitParams sp) {
-  constexpr int NT = kSplitThreads;
-  constexpr int KC = kSplitStrips;
-  constexpr int W = kSplitCols;                     // slice width (elements)
+template <int NORM, class IN, int SH>
+__global__ __launch_bounds__(kSplitShapes[SH].threads) void fwd_split_kernel(FwdSplitParams sp) {
+  constexpr int NT = kSplitShapes[SH].threads;
+  constexpr int KC = kSplitShapes[SH].strips;
+  constexpr int W = (int)kSplitShapes[SH].cols();  // slice width (elements)
+  constexpr bool WREG = kSplitShapes[SH].wreg != 0; // gamma in registers, beta in LDS
+  constexpr int DEPTH = kSplitShapes[SH].depth;     // rows in flight
+  static_assert(DEPTH == 3 || DEPTH == 4, "split pipeline depth");
   constexpr int NW = NORM == NT_LAYERNORM ? 2 : 1;  // weight arrays
   constexpr int NV = NORM == NT_LAYERNORM ? 3 : 1;  // tagged words per slice partial
   constexpr int NWAVE = NT / 64;
@@ -48,7 +55,10 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(FwdSplitParams
   const int64_t N = p.rows;
   const int S = sp.S;
 
-  __shared__ float wlds[NW * W];
+  // LDS weights: [gamma][beta] (shape 0) or [beta] (register gamma; LayerNorm)
+  constexpr int WL_FLOATS = WREG ? (NORM == NT_LAYERNORM ? W : 1) : NW * W;
+  constexpr int BETA_OFF = WREG ? 0 : W;
+  __shared__ __align__(16) float wlds[WL_FLOATS];
   __shared__ ShiftedStats wpart[2][NWAVE];
   __shared__ uint32_t s_ticket, s_epoch, s_last;
 
@@ -66,19 +76,38 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(FwdSplitParams
   const int cols = (int)(H - c0 < W ? H - c0 : W);  // columns of this slice
 
   // ---- the slice's weights, once
+  float gr[WREG ? KC : 1][8];  // register gamma (shape 1): strip k's 8 weights, zero past the slice
+  if constexpr (WREG) {
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int c = 8 * (tid + NT * k);
+      if (c < cols) {
+        load_w8(gr[k], p.gamma, c0 + c, p.w_dtype);
+        if (p.zero_centered) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) gr[k][i] += 1.0f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gr[k][i] = 0.0f;
+      }
+    }
+  }
   for (int c = 8 * tid; c < cols; c += 8 * NT) {
     float w[8];
-    load_w8(w, p.gamma, c0 + c, p.w_dtype);
-    if (p.zero_centered) {
+    if constexpr (!WREG) {
+      load_w8(w, p.gamma, c0 + c, p.w_dtype);
+      if (p.zero_centered) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] += 1.0f;
+        for (int i = 0; i < 8; ++i) w[i] += 1.0f;
+      }
+      float4 *d = reinterpret_cast<float4 *>(wlds + c);
+      d[0] = make_float4(w[0], w[1], w[2], w[3]);
+      d[1] = make_float4(w[4], w[5], w[6], w[7]);
     }
-    float4 *d = reinterpret_cast<float4 *>(wlds + c);
-    d[0] = make_float4(w[0], w[1], w[2], w[3]);
-    d[1] = make_float4(w[4], w[5], w[6], w[7]);
     if constexpr (NORM == NT_LAYERNORM) {
       load_w8(w, p.beta, c0 + c, p.w_dtype);
-      float4 *e = reinterpret_cast<float4 *>(wlds + W + c);
+      float4 *e = reinterpret_cast<float4 *>(wlds + BETA_OFF + c);
       e[0] = make_float4(w[0], w[1], w[2], w[3]);
       e[1] = make_float4(w[4], w[5], w[6], w[7]);
     }
@@ -223,13 +252,19 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(FwdSplitParams
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       const int c = 8 * (tid + NT * k);
-      float xv[8], y[8];
+      float xv[8], y[8], gk[8];
       strip_to_f32<IN>(b[k], xv);
-      const float4 *g4 = reinterpret_cast<const float4 *>(wlds + c);
-      const float4 ga = g4[0], gb = g4[1];
-      const float gk[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      if constexpr (WREG) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gk[i] = gr[k][i];
+      } else {
+        const float4 *g4 = reinterpret_cast<const float4 *>(wlds + c);
+        const float4 ga = g4[0], gb = g4[1];
+        gk[0] = ga.x; gk[1] = ga.y; gk[2] = ga.z; gk[3] = ga.w;
+        gk[4] = gb.x; gk[5] = gb.y; gk[6] = gb.z; gk[7] = gb.w;
+      }
       if constexpr (NORM == NT_LAYERNORM) {
-        const float4 *b4 = reinterpret_cast<const float4 *>(wlds + W + c);
+        const float4 *b4 = reinterpret_cast<const float4 *>(wlds + BETA_OFF + c);
         const float4 ba = b4[0], bb = b4[1];
         const float bk[8] = {ba.x, ba.y, ba.z, ba.w, bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
@@ -243,33 +278,54 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(FwdSplitParams
     }
   };
 
-  // three row buffers in turn: row j + 2 loads while row j + 1 is reduced and published and
-  // row j finishes
-  // four row buffers in turn: row j + 3 loads while row j + 2 is reduced and published and row
-  // j finishes with the words loaded one row earlier (two rows after their publication)
-  RowBuf A, B, C, D;
-  load_row(A, 0);
-  load_row(B, 1);
-  load_row(C, 2);
-  stats_publish(A, 0);
-  stats_publish(B, 1);
-  uint64_t pv = poll_issue(0);
-  for (int64_t j = 0; j < nr; j += 4) {
-    load_row(D, j + 3);
-    stats_publish(C, j + 2);
-    finish(A, j, pv);
-    if (j + 1 >= nr) break;
-    load_row(A, j + 4);
-    stats_publish(D, j + 3);
-    finish(B, j + 1, pv);
-    if (j + 2 >= nr) break;
-    load_row(B, j + 5);
-    stats_publish(A, j + 4);
-    finish(C, j + 2, pv);
-    if (j + 3 >= nr) break;
-    load_row(C, j + 6);
-    stats_publish(B, j + 5);
-    finish(D, j + 3, pv);
+  if constexpr (DEPTH == 4) {
+    // four row buffers in turn: row j + 3 loads while row j + 2 is reduced and published and
+    // row j finishes with the words loaded one row earlier (two rows after their publication)
+    RowBuf A, B, C, D;
+    load_row(A, 0);
+    load_row(B, 1);
+    load_row(C, 2);
+    stats_publish(A, 0);
+    stats_publish(B, 1);
+    uint64_t pv = poll_issue(0);
+    for (int64_t j = 0; j < nr; j += 4) {
+      load_row(D, j + 3);
+      stats_publish(C, j + 2);
+      finish(A, j, pv);
+      if (j + 1 >= nr) break;
+      load_row(A, j + 4);
+      stats_publish(D, j + 3);
+      finish(B, j + 1, pv);
+      if (j + 2 >= nr) break;
+      load_row(B, j + 5);
+      stats_publish(A, j + 4);
+      finish(C, j + 2, pv);
+      if (j + 3 >= nr) break;
+      load_row(C, j + 6);
+      stats_publish(B, j + 5);
+      finish(D, j + 3, pv);
+    }
+  } else {
+    // three row buffers in turn: row j + 2 loads while row j + 1 is reduced and published and
+    // row j finishes with the words published one row earlier
+    RowBuf A, B, C;
+    load_row(A, 0);
+    load_row(B, 1);
+    stats_publish(A, 0);
+    uint64_t pv = poll_issue(0);
+    for (int64_t j = 0; j < nr; j += 3) {
+      load_row(C, j + 2);
+      stats_publish(B, j + 1);
+      finish(A, j, pv);
+      if (j + 1 >= nr) break;
+      load_row(A, j + 3);
+      stats_publish(C, j + 2);
+      finish(B, j + 1, pv);
+      if (j + 2 >= nr) break;
+      load_row(B, j + 4);
+      stats_publish(A, j + 3);
+      finish(C, j + 2, pv);
+    }
   }
 
   // ---- end of launch: the last workgroup re-zeroes the ticket counter and advances the epoch
@@ -283,17 +339,26 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(FwdSplitParams
 }
 
 template <int NORM>
-static const void *pick_split_in(int in_dtype) {
+static const void *pick_split_in(int in_dtype, int shape) {
+  if (shape == 1) {  // (16-bit input only: three float32 rows would not fit beside gamma)
+    switch (in_dtype) {
+      case DT_BF16: return (const void *)fwd_split_kernel<NORM, BF16, 1>;
+      case DT_F16: return (const void *)fwd_split_kernel<NORM, F16, 1>;
+      default: return nullptr;
+    }
+  }
+  if (shape != 0) return nullptr;
   switch (in_dtype) {
-    case DT_F32: return (const void *)fwd_split_kernel<NORM, F32>;
-    case DT_BF16: return (const void *)fwd_split_kernel<NORM, BF16>;
-    case DT_F16: return (const void *)fwd_split_kernel<NORM, F16>;
+    case DT_F32: return (const void *)fwd_split_kernel<NORM, F32, 0>;
+    case DT_BF16: return (const void *)fwd_split_kernel<NORM, BF16, 0>;
+    case DT_F16: return (const void *)fwd_split_kernel<NORM, F16, 0>;
     default: return nullptr;
   }
 }
 
-const void *fwd_split_kernel_ptr(int norm, int in_dtype) {
-  return norm == NT_LAYERNORM ? pick_split_in<NT_LAYERNORM>(in_dtype) : pick_split_in<NT_RMSNORM>(in_dtype);
+const void *fwd_split_kernel_ptr(int norm, int in_dtype, int shape) {
+  return norm == NT_LAYERNORM ? pick_split_in<NT_LAYERNORM>(in_dtype, shape)
+                              : pick_split_in<NT_RMSNORM>(in_dtype, shape);
 }
 
 }  // namespace nf8

@@ -76,11 +76,16 @@ constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1, 4}, {4, 1, 2}, {4, 2, 2}, {8, 
                                            {16, 2, 1}, {8, 1, 1}, {16, 1, 1}, {4, 4, 1},
                                            {2, 1, 1}, {4, 1, 1}, {4, 2, 1}, {8, 3, 1}};
 
-// ---- forward split kernel: 16 waves, two 16-byte strips per lane: a 16384-column slice
-constexpr int kSplitThreads = 1024;
-constexpr int kSplitStrips = 2;
-constexpr int kSplitCols = 8 * kSplitThreads * kSplitStrips;
-constexpr int kSplitMaxSlices = 8;  // rows up to 131072 elements
+// ---- forward split kernel: S workgroups per row, each holding one slice of every row of its row
+// group. Shape 0 (any input dtype): 16 waves x 2 strips, a 16384-column slice, its weights in
+// LDS, four rows in flight. Shape 1 (16-bit input): 8 waves x 8 strips, a 32768-column slice,
+// gamma in registers and beta (LayerNorm) in LDS, three rows in flight.
+struct SplitShape {
+  int threads, strips, wreg, depth;
+  constexpr int64_t cols() const { return 8LL * threads * strips; }
+};
+constexpr SplitShape kSplitShapes[2] = {{1024, 2, 0, 4}, {512, 8, 1, 3}};
+constexpr int kSplitMaxSlices = 8;  // shape 0: rows up to 131072 elements; shape 1: 262144
 
 // ---- single-pass columnwise kernel: 8 waves, 128-row bands of 512-column slices
 constexpr int kColxThreads = 512;
@@ -94,7 +99,7 @@ constexpr int kColThreads = 4 * kColTileRows;  // 16 rows per wave
 
 const void *fwd_row_kernel_ptr(int norm, int in_dtype, int mode, int cfg);
 const void *fwd_band_kernel_ptr(int norm, int in_dtype, int mode, bool col, int cfg);
-const void *fwd_split_kernel_ptr(int norm, int in_dtype);
+const void *fwd_split_kernel_ptr(int norm, int in_dtype, int shape);  // shape 1: 16-bit input only
 const void *fwd_colx_kernel_ptr(int in_dtype, int out_dtype, int mode);  // RMSNorm only
 const void *fwd_tile_kernel_ptr(int norm, int in_dtype, int mode, bool col_rowmajor);
 // tiles of 32 * rows_per_lane rows x 256 columns (rows_per_lane 4 or 8), or of 512 rows x 128

@@ -644,20 +644,24 @@ def test_fwd_then_bwd_end_to_end():
 # ------------------------------------------------------------------------------ split rows
 
 SPLIT_SHAPES = [(3, 8), (5, 4096), (37, 16384), (9, 16392), (300, 40000), (2, 65536), (70, 65536),
-                (4, 131072), (1, 98304)]
+                (4, 131072), (1, 98304), (520, 65536)]
 
 
+@pytest.mark.parametrize("shape", [0, 1])
 @pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
 @pytest.mark.parametrize("in_dt", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("rows,hidden", SPLIT_SHAPES)
-def test_fwd_split_rows(norm, in_dt, rows, hidden):
-    """The split kernel (S = ceil(hidden / 16384) workgroups per row, weight slices in LDS,
-    tagged partial exchange), forced on every shape: one to eight slices, ragged last slices,
-    fewer rows than row groups."""
+def test_fwd_split_rows(norm, in_dt, rows, hidden, shape):
+    """The split kernel (S = ceil(hidden / W) workgroups per row, tagged partial exchange),
+    forced on every shape: one to eight slices, ragged last slices, fewer rows than row groups
+    and several rows per group. Shape 0: 16384-column slices with the weights in LDS, four rows
+    in flight; shape 1 (16-bit input; float32 input stays on shape 0): 32768-column slices with
+    gamma in registers and beta in LDS, three rows in flight."""
     case = workloads.small_case(norm, rows, hidden, in_dt, "f32", seed=rows + hidden + 11)
     ref = oracle_fwd(case, norm, in_dt, "f32", False)
     x, g, b = gpu(case, "x", "gamma", "beta")
-    with env(NORMFP8_SPLIT=1):
+    print(f"split: shape {shape} {norm} {in_dt} {rows}x{hidden}", flush=True)
+    with env(NORMFP8_SPLIT=1, NORMFP8_SPLIT_SHAPE=shape):
         out = nf.fwd(x, g, b, norm=norm, eps=EPS)
     checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
                        out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
@@ -665,14 +669,15 @@ def test_fwd_split_rows(norm, in_dt, rows, hidden):
     assert_ws_clean()
 
 
+@pytest.mark.parametrize("shape", [0, 1])
 @pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
-def test_fwd_split_zero_centered_bf16_weights_and_margin(norm):
+def test_fwd_split_zero_centered_bf16_weights_and_margin(norm, shape):
     rows, hidden = 33, 49152
     case = workloads.small_case(norm, rows, hidden, "bf16", "bf16", seed=5, zero_centered_gamma=True)
     ref = oracle_fwd(case, norm, "bf16", "bf16", True)
     x, g, b = gpu(case, "x", "gamma", "beta")
     for margin in (0, 200, 250):
-        with env(NORMFP8_SPLIT=1):
+        with env(NORMFP8_SPLIT=1, NORMFP8_SPLIT_SHAPE=shape):
             out = nf.fwd(x, g, b, norm=norm, eps=EPS, zero_centered_gamma=True, cu_margin=margin)
         checks.check_stats(out["mu"].cpu().numpy() if out["mu"] is not None else None,
                            out["rsigma"].cpu().numpy(), ref["mu"], ref["rsigma"])
@@ -802,7 +807,7 @@ def test_fwd_colx_matches_two_pass_statistics():
 
 def test_repeat_runs_are_bitwise_identical():
     """Repeated calls give the same bytes: the band split (forced: its cross-workgroup exchange
-    of row partials through tagged words and tickets), the split kernel, the columnwise tile path,
+    of row partials through tagged words and tickets), both split kernel shapes, the columnwise tile path,
     the single-pass columnwise band kernel, the single-pass RMSNorm columnwise kernel (row sums
     exchanged between 512-column slices; MXFP8 and delayed) and the backward's fixed-order partial
     reduction."""
@@ -810,6 +815,8 @@ def test_repeat_runs_are_bitwise_identical():
     dy, x, g, b = gpu(case, "dy", "x", "gamma", "beta")
     xs, dys, gs = x[:, :16384].contiguous(), dy[:, :16384].contiguous(), g[:16384].contiguous()
     xr, gr = x[:384, :6144].contiguous(), g[:6144].contiguous()   # 3 super-bands x 12 slices
+    wide = workloads.small_case("layernorm", 300, 40000, "bf16", "f32", seed=9)
+    xw, gw, bw = gpu(wide, "x", "gamma", "beta")
     st = torch.tensor([16.0], device="cuda")
     outs = []
     for _ in range(3):
@@ -821,13 +828,16 @@ def test_repeat_runs_are_bitwise_identical():
                   fd["y"], fd["y_colwise"], fd["amax"], fd["rsigma"]]
         with env(NORMFP8_FORCE_BAND=1, NORMFP8_SPLIT=0):
             f = nf.fwd(x, g, b, norm="layernorm")                  # band split (20480 columns)
-        with env(NORMFP8_SPLIT=1):
+        with env(NORMFP8_SPLIT=1, NORMFP8_SPLIT_SHAPE=0):
             fs = nf.fwd(x, g, b, norm="layernorm")                 # split kernel (two slices)
+        with env(NORMFP8_SPLIT=1, NORMFP8_SPLIT_SHAPE=1):
+            fs1 = nf.fwd(xw, gw, bw, norm="layernorm")             # 8-wave split shape (two slices)
         with env(NORMFP8_COL_KERNEL=0):
             fb = nf.fwd(x, g, b, norm="layernorm", scaling="mxfp8", layout="rowwise_colwise")
         fc = nf.fwd(x, g, b, norm="layernorm", scaling="mxfp8", layout="rowwise_colwise")
         d = nf.bwd(dys, xs, f["mu"], f["rsigma"], gs, norm="layernorm")
         outs.append([t.clone() for t in (f["y"], f["mu"], f["rsigma"], fs["y"], fs["mu"], fs["rsigma"],
+                                          fs1["y"], fs1["mu"], fs1["rsigma"],
                                           fb["y"], fb["y_colwise"], fb["rsigma"],
                                           fc["y"], fc["y_colwise"], fc["colwise_scale_inv"],
                                           d["dx"], d["dgamma"], d["dbeta"], *outs_x)])
