@@ -261,6 +261,11 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
     // from the caches per strip (bf16 2048 x 32768: 76 -> 54 us; 4096 x 16392: 105 -> 69 us)
     if (norm_type == NORM_LAYERNORM && row_cfg == ROW_W16_K4 && pl->mode == MODE_PLAIN && in_dtype != DT_F32)
       row_cfg = ROW_W8_K8;
+    // and rows of 8193..16384: 4 waves with gamma and beta in registers, where the two rows of 8
+    // waves sharing 128 KB of LDS weights read those 128 KB from LDS for every row (bf16 16384 x
+    // 12288: 163-168 -> 149 us; 19660 x 10240: 184-189 -> 152 us; 12288 x 16384: 152 -> 143.5 us)
+    if (norm_type == NORM_LAYERNORM && row_cfg == ROW_W8T2_K4 && pl->mode == MODE_PLAIN && in_dtype != DT_F32)
+      row_cfg = ROW_W4_K8;
   }
   // a columnwise output goes through the statistics pass + tile kernel when a row layout covers
   // the row (NORMFP8_COL_KERNEL=0 selects the single-pass band kernel instead)

@@ -414,11 +414,15 @@ static const void *pick_cfg(int cfg) {
     // LayerNorm's gamma and beta would need 64 and spill, so they are read per strip
     case ROW_W16_K4:
       return (const void *)fwd_row_kernel<NORM, IN, MODE, 16, 1, 4, NORM == NT_LAYERNORM ? 2 : 0>;
-    // weights in registers for the whole persistent workgroup (LayerNorm: 128 per lane, 244
-    // VGPRs at 8 waves); the FP8 epilogues and float32 input would spill there
+    // weights in registers for the whole persistent workgroup (LayerNorm: 128 per lane, 244-248
+    // VGPRs); the FP8 epilogues and float32 input would spill there
     case ROW_W8_K8:
       if constexpr ((MODE == MODE_PLAIN || MODE == MODE_STATS) && IN::bytes == 2)
         return (const void *)fwd_row_kernel<NORM, IN, MODE, 8, 1, 8, 0>;
+      return nullptr;
+    case ROW_W4_K8:
+      if constexpr ((MODE == MODE_PLAIN || MODE == MODE_STATS) && IN::bytes == 2)
+        return (const void *)fwd_row_kernel<NORM, IN, MODE, 4, 1, 8, 0>;
       return nullptr;
     default: return nullptr;
   }

@@ -26,6 +26,8 @@ enum RowCfg : int {
   ROW_W8_K8,    // 8 waves per row, 8 strips per lane, gamma and beta in registers (LayerNorm rows of
                 // 16385..32768, 16-bit input, no FP8 epilogue; instantiated for 16-bit plain and
                 // statistics-only passes only)
+  ROW_W4_K8,    // 4 waves per row, 8 strips per lane, gamma and beta in registers (LayerNorm rows of
+                // 8193..16384, the same instances)
   ROW_NCFG
 };
 struct RowShape {
@@ -35,7 +37,7 @@ struct RowShape {
 };
 constexpr RowShape kRowShapes[ROW_NCFG] = {{1, 4, 1}, {1, 4, 2}, {1, 4, 4}, {1, 4, 8}, {4, 1, 2}, {4, 1, 4},
                                            {8, 1, 4}, {2, 2, 4}, {8, 1, 1}, {4, 2, 2}, {16, 1, 8},
-                                           {4, 4, 4}, {16, 1, 2}, {8, 2, 4}, {16, 1, 4}, {8, 1, 8}};
+                                           {4, 4, 4}, {16, 1, 2}, {8, 2, 4}, {16, 1, 4}, {8, 1, 8}, {4, 1, 8}};
 
 // ---- forward band kernel: 4 waves, RW rows per wave, KC strips per lane
 enum BandCfg : int { BAND_R8_K1 = 0, BAND_R8_K2, BAND_R4_K2, BAND_R1_K4, BAND_R2_K8, BAND_NCFG };
