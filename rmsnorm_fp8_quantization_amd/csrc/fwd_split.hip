@@ -16,9 +16,9 @@
 // for 16-bit input, 8 waves x 8 strips (W = 32768) with gamma in registers (64 per lane), beta in
 // LDS (128 KB) and three rows in flight.
 //
-// Per row: every wave reduces its 1024 elements (LayerNorm: deviations from the wave's plain
-// mean estimate, so that a large common part of the row costs no precision), the 16 wave
-// partials are merged through LDS in wave order, and the slice's partial is published to the
+// Per row: every wave reduces its elements of the slice (1024 or 4096; LayerNorm: deviations
+// from the wave's plain mean estimate, so that a large common part of the row costs no
+// precision), the waves' partials are merged through LDS in wave order, and the slice's partial is published to the
 // workspace as tagged 64-bit words {value, launch tag}. Each workgroup then polls the S slices'
 // words of the row and merges them in slice order, so all S workgroups obtain identical
 // statistics. Four rows are in flight: row j + 3 is loading and row j + 2 publishes its partial
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kSplitShapes[SH].threads) void fwd_split_kernel(Fwd
       Stats st = wpart[j & 1][0].s;
       const float k0 = wpart[j & 1][0].k;
 #pragma unroll 1
-      for (int w = 1; w < NWAVE; ++w) {  // (not unrolled: sixteen partials read ahead would take 64 registers)
+      for (int w = 1; w < NWAVE; ++w) {  // (not unrolled: the partials read ahead would take 4 registers each)
         const ShiftedStats o = wpart[j & 1][w];
         if constexpr (NORM == NT_LAYERNORM) st = chan_merge(st, in_frame(o, k0));
         else st.m2 += o.s.m2;

@@ -92,8 +92,9 @@ struct FwdBandParams {
 };
 
 // ---- forward split kernel (long rows) -------------------------------------------------------
-// S workgroups per row group, each holding one 16384-column slice of every row of the group and
-// that slice's weights in LDS; per row the slices exchange tagged partial statistics
+// S workgroups per row group, each holding one slice (16384 or 32768 columns, by shape) of every
+// row of the group and that slice's weights (LDS, or gamma in registers); per row the slices
+// exchange tagged partial statistics
 // (LayerNorm: mean and M2 relative to a shift, and the shift; RMSNorm: the sum of squares).
 struct FwdSplitParams {
   FwdRowParams f;        // y = the output
