@@ -225,6 +225,32 @@ int norm_workspace_init(void *stream, void *workspace, size_t workspace_bytes);
  */
 int norm_workspace_check(void *stream, void *workspace, uint32_t *flags);
 
+/* The kernels a forward request goes to (norm_fwd_launch_shape). */
+typedef enum {
+  NORM_ROUTE_ROW = 0,               /* row kernel: one team of waves per row */
+  NORM_ROUTE_ROW_TRANSPOSE = 1,     /* row kernel, then a byte transpose of its codes (delayed, both outputs) */
+  NORM_ROUTE_STATS_TILES = 2,       /* statistics pass of the row kernel, then 128 x 128 tiles */
+  NORM_ROUTE_BAND = 3,              /* band kernel: row tiles over S workgroups */
+  NORM_ROUTE_SPLIT = 4,             /* split kernel: long rows over S workgroups */
+  NORM_ROUTE_SINGLE_PASS_COLWISE = 5, /* single-pass columnwise kernel (RMSNorm FP8) */
+  NORM_ROUTE_GENERAL = 6            /* general kernels (any hidden size) */
+} norm_fwd_route_t;
+
+/*
+ * Planner query, host only (no GPU needed): the kernels norm_fwd chooses for these arguments
+ * (those of norm_fwd_workspace_size that steer the plan). On return shape[0] = route
+ * (norm_fwd_route_t); shape[1] = layout index (the row layout for routes ROW, ROW_TRANSPOSE and
+ * STATS_TILES, the band layout for BAND, the split kernel's shape for SPLIT, else 0); shape[2] =
+ * waves per row, shape[3] = 16-byte strips per lane and shape[4] = rows per workgroup of that row
+ * layout (0 for other routes); shape[5] = S, the workgroups that share a row (BAND, SPLIT,
+ * SINGLE_PASS_COLWISE; else 1). Tensors aligned only to their element size send a request to the
+ * general kernels at launch, which this query does not see. [NVRTC-PR] Description and Flowchart
+ * (the tuned kernel chosen per row length, the general kernel otherwise). For tests of the
+ * planner's choices.
+ */
+int norm_fwd_launch_shape(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
+                          int scaling, int qlayout, int cu_margin, int64_t shape[6]);
+
 /*
  * Planner query, host only (no GPU needed): the launch shape norm_bwd / norm_bwd_add choose for
  * these arguments on a device with `cu_count` compute units, `cu_margin` of them left free,

@@ -22,10 +22,13 @@ NORM_F32, NORM_F16, NORM_BF16, NORM_FP8_E4M3, NORM_FP8_E5M2 = range(5)
 NORM_SCALING_NONE, NORM_SCALING_DELAYED_TENSOR, NORM_SCALING_MXFP8_1D32, NORM_SCALING_MXFP8_1D32_CEIL = range(4)
 NORM_Q_ROWWISE, NORM_Q_COLWISE, NORM_Q_ROWWISE_COLWISE, NORM_Q_COLWISE_ROWMAJOR = 1, 2, 3, 4
 NORM_Q_SCALES_PADDED = 8
+(NORM_ROUTE_ROW, NORM_ROUTE_ROW_TRANSPOSE, NORM_ROUTE_STATS_TILES, NORM_ROUTE_BAND, NORM_ROUTE_SPLIT,
+ NORM_ROUTE_SINGLE_PASS_COLWISE, NORM_ROUTE_GENERAL) = range(7)
 NORM_WS_HEADER_BYTES = 16384
 
 EXPORTS = ("norm_fwd_workspace_size", "norm_bwd_workspace_size", "norm_fwd", "norm_bwd",
            "norm_bwd_add", "norm_bwd_noalloc", "norm_workspace_init", "norm_workspace_check", "norm_bwd_launch_shape",
+           "norm_fwd_launch_shape",
            "norm_tuning_set", "norm_last_error", "norm_abi_version")
 ABI_VERSION = 2
 KNOB_UNSET = -2 ** 31  # INT_MIN: a tuning override that is not set
@@ -47,6 +50,7 @@ _SIGS = {
     "norm_workspace_init": [_P, _P, _SZ],
     "norm_workspace_check": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
     "norm_bwd_launch_shape": [_I64, _I64, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I64)],
+    "norm_fwd_launch_shape": [_I64, _I64, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I64)],
     "norm_tuning_set": [ctypes.c_char_p, _I, ctypes.POINTER(_I)],
     "norm_last_error": [],
     "norm_abi_version": [],

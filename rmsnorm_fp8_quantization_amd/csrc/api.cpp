@@ -173,7 +173,7 @@ struct FwdPlan {
   bool scales_padded = false;  // MXFP8 E8M0 grids padded (block dimension to 4, the other to 128)
   bool tr = false;    // delayed scaling, rowwise + columnwise: row kernel, then a byte transpose
   bool gen = false;   // general kernels: hidden not a multiple of 8 (or, at launch, unaligned tensors)
-  bool split = false; // long rows, no FP8 epilogue: the split kernel (S slices per row, weights in LDS)
+  bool split = false; // long rows, no FP8 epilogue: the split kernel (S slices per row)
   int split_shape = 0; // the split kernel's shape (kSplitShapes)
   bool colx = false;  // RMSNorm FP8 with a columnwise output: the single-pass band-exchange kernel
 };
@@ -985,6 +985,40 @@ int norm_bwd_add(void *stream, const void *dy, const void *x, const void *residu
   return bwd_common(stream, true, dy, x, residual_dy, nullptr, rsigma, gamma, dx, dgamma, nullptr, workspace,
                     workspace_bytes, rows, hidden, in_dtype, w_dtype, NORM_RMSNORM, zero_centered_gamma,
                     cu_margin);
+}
+
+int norm_fwd_launch_shape(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
+                          int scaling, int qlayout, int cu_margin, int64_t shape[6]) {
+  if (!shape) return fail(NORM_ERR_INVALID_ARG, "shape is NULL");
+  FwdPlan pl;
+  int rc = plan_fwd(rows, hidden, in_dtype, w_dtype, out_dtype, norm_type, scaling, qlayout, cu_margin, &pl);
+  if (rc) return rc;
+  for (int i = 0; i < 6; ++i) shape[i] = 0;
+  shape[5] = 1;
+  int route;
+  if (pl.gen) route = NORM_ROUTE_GENERAL;
+  else if (pl.colx) route = NORM_ROUTE_SINGLE_PASS_COLWISE;
+  else if (pl.split) route = NORM_ROUTE_SPLIT;
+  else if (pl.band) route = NORM_ROUTE_BAND;
+  else if (pl.col) route = pl.tr ? NORM_ROUTE_ROW_TRANSPOSE : NORM_ROUTE_STATS_TILES;
+  else route = NORM_ROUTE_ROW;
+  shape[0] = route;
+  if (route == NORM_ROUTE_ROW || route == NORM_ROUTE_ROW_TRANSPOSE || route == NORM_ROUTE_STATS_TILES) {
+    const RowShape &sh = kRowShapes[pl.cfg];
+    shape[1] = pl.cfg;
+    shape[2] = sh.P;
+    shape[3] = sh.KC;
+    shape[4] = sh.T;
+  } else if (route == NORM_ROUTE_BAND) {
+    shape[1] = pl.cfg;
+    shape[5] = pl.S;
+  } else if (route == NORM_ROUTE_SPLIT) {
+    shape[1] = pl.split_shape;
+    shape[5] = pl.S;
+  } else if (route == NORM_ROUTE_SINGLE_PASS_COLWISE) {
+    shape[5] = pl.S;
+  }
+  return ok();
 }
 
 int norm_bwd_launch_shape(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_type, int with_add,
