@@ -23,7 +23,9 @@ template <int NORM, class IN, bool ADD, int W, int KC, int T>
 __global__ __launch_bounds__(64 * W * T) void bwd_kernel(BwdParams p) {
   constexpr int NT = 64 * W;  // threads of one team (one row)
   const int lane = threadIdx.x & 63;
-  const int team = (int)threadIdx.x / NT;
+  // (the team is the same for every lane of a wave: taken through readfirstlane so that row
+  // indices and row addresses are scalar)
+  const int team = __builtin_amdgcn_readfirstlane((int)threadIdx.x / NT);
   const int tid = (int)threadIdx.x - team * NT;  // thread within the team
   const int wave = tid >> 6;                      // wave within the team
   const int64_t H = p.hidden;
@@ -54,23 +56,30 @@ __global__ __launch_bounds__(64 * W * T) void bwd_kernel(BwdParams p) {
   __shared__ float red[2][T][W][2];
   const float inv_h = 1.0f / (float)H;
 
-  // The next row's dy, x (and residual) are loaded while the current row is processed. The
-  // loads are unconditional (a row past the end reads row 0, a strip past the end of the row
-  // reads column 0) and masked where they are used: under a branch a load may not have been
-  // issued, and the wait before the current row's first use would then drain the prefetch too.
+  // The next row's dy, x (and residual) are loaded while the current row is processed. Every
+  // load and store is issued on every path (buffer accesses whose offset is moved past the
+  // row's end where a lane has nothing to read or write): under a branch an access may not
+  // have been issued, and the wait before the next use of an earlier load would then drain
+  // every access in flight, the next row's loads included.
   struct RowData {
     Strip<IN> dys[KC], xs[KC], rsd[ADD ? KC : 1];
     float rs, mu;
   };
+  // (a strip past the end of the row, or of a row past the last, reads zeros)
+  const uint32_t row_bytes = (uint32_t)(H * IN::bytes);
   auto load_row = [&](RowData &d, int64_t base) {
     const int64_t row = base + team;
-    const int64_t r = row < p.rows ? row : 0;
+    const bool in = row < p.rows;
+    const int64_t r = in ? row : 0;
+    const nf8_rsrc rdy = make_rsrc(static_cast<const char *>(p.dy) + r * row_bytes, row_bytes);
+    const nf8_rsrc rx = make_rsrc(static_cast<const char *>(p.x) + r * row_bytes, row_bytes);
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      const int64_t off = r * H + (cv[k] ? 8 * (int64_t)(tid + NT * k) : 0);
-      load_strip<IN>(d.dys[k], p.dy, off);
-      load_strip<IN>(d.xs[k], p.x, off);
-      if constexpr (ADD) load_strip<IN>(d.rsd[k], p.residual, off);
+      const uint32_t off = in && cv[k] ? (uint32_t)(8 * IN::bytes * (tid + NT * k)) : kOffNone;
+      load_strip_at<IN>(d.dys[k], rdy, off);
+      load_strip_at<IN>(d.xs[k], rx, off);
+      if constexpr (ADD)
+        load_strip_at<IN>(d.rsd[k], make_rsrc(static_cast<const char *>(p.residual) + r * row_bytes, row_bytes), off);
     }
     d.rs = p.rsigma[r];
     d.mu = NORM == NT_LAYERNORM ? p.mu[r] : 0.0f;
@@ -80,15 +89,6 @@ __global__ __launch_bounds__(64 * W * T) void bwd_kernel(BwdParams p) {
   auto step = [&](RowData &cur, int64_t base, int iter) {
     const int64_t row = base + team;
     const bool rv = row < p.rows;  // a team past the last row adds nothing and stores nothing
-#pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      if (!cv[k]) {
-        zero_strip<IN>(cur.dys[k]);
-        zero_strip<IN>(cur.xs[k]);
-        if constexpr (ADD) zero_strip<IN>(cur.rsd[k]);
-      }
-      if constexpr (T > 1) mask_strip<IN>(cur.dys[k], rv);
-    }
     const Strip<IN> *const dys = cur.dys;
     const Strip<IN> *const xs = cur.xs;
     const Strip<IN> *const rsd = cur.rsd;
@@ -126,6 +126,9 @@ __global__ __launch_bounds__(64 * W * T) void bwd_kernel(BwdParams p) {
         s2 += red[iter & 1][team][w][1];
       }
     }
+    // dx of this row through a resource that covers the row (the team's row is the same for
+    // every lane of a wave)
+    const nf8_rsrc rdx = make_rsrc(static_cast<char *>(p.dx) + (rv ? row : 0) * row_bytes, row_bytes);
     const float c1 = NORM == NT_LAYERNORM ? s1 * inv_h : 0.0f;
     const float c2 = s2 * inv_h;
 
@@ -146,27 +149,50 @@ __global__ __launch_bounds__(64 * W * T) void bwd_kernel(BwdParams p) {
         dg[k][i] = fmaf(dv[i], xh, dg[k][i]);
         if constexpr (NORM == NT_LAYERNORM) db[k][i] += dv[i];
       }
-      if (rv && cv[k]) store_t8<IN>(p.dx, row * H + 8 * (int64_t)(tid + NT * k), out);
+      store_t8_at<IN>(rdx, rv && cv[k] ? (uint32_t)(8 * IN::bytes * (tid + NT * k)) : kOffNone, out);
     }
   };
 
   // Two row buffers used in turn, so that the next row's loads never wait on the current
-  // row's registers. (Not for 16 waves x 2 strips: two rows of inputs would not fit the
-  // register budget; those load each row after the previous one is done.)
-  constexpr bool PF = !(W == 16 && KC >= 2);
+  // row's registers. (Not for 16 waves x 2 strips, nor for float32 rows of 3 strips per lane:
+  // two rows of inputs would not fit the register budget; those load each row after the
+  // previous one is done.)
+  constexpr bool PF = !(W == 16 && KC >= 2) && !(IN::bytes == 4 && KC >= 3);
   // (T teams walk rows base + team in step, so every team makes the same number of steps and
   // meets every barrier)
+  // The workgroup's n steps (base rows first, first + G, ...) run as n / 2 two-step trips and
+  // a last single step: a loop with one exit (a break between the two steps would join the
+  // back edge on a path where the next row's loads are never used, and every trip would then
+  // wait for all accesses in flight before issuing its loads).
   const int64_t G = (int64_t)gridDim.x * T;
+  const int64_t first = (int64_t)blockIdx.x * T;
+  const int64_t n = first < p.rows ? (p.rows - first + G - 1) / G : 0;
   RowData a, b;
-  load_row(a, (int64_t)blockIdx.x * T);
-  for (int64_t row = (int64_t)blockIdx.x * T, iter = 0; row < p.rows; row += 2 * G, iter += 2) {
-    if constexpr (PF) load_row(b, row + G);
-    step(a, row, (int)iter);
-    if (row + G >= p.rows) break;
-    if constexpr (PF) load_row(a, row + 2 * G);
-    else load_row(b, row + G);
-    step(b, row + G, (int)iter + 1);
-    if constexpr (!PF) load_row(a, row + 2 * G);
+  load_row(a, first);
+  int64_t row = first;
+  int iter = 0;
+  if constexpr (PF) {
+    for (int64_t q = n >> 1; q > 0; --q) {
+      // (the scheduling barriers keep each row's work below the next row's loads: work on a
+      // row moved above them would make the loads wait for that row's own loads)
+      load_row(b, row + G);
+      __builtin_amdgcn_sched_barrier(0);
+      step(a, row, iter);
+      load_row(a, row + 2 * G);
+      __builtin_amdgcn_sched_barrier(0);
+      step(b, row + G, iter + 1);
+      row += 2 * G;
+      iter += 2;
+    }
+    if (n & 1) step(a, row, iter);
+  } else {
+    // one buffer: each row's loads go out after the previous row is done
+    for (int64_t q = n; q > 0; --q) {
+      step(a, row, iter);
+      load_row(a, row + G);
+      row += G;
+      ++iter;
+    }
   }
 
   // the teams' weight-gradient sums, added in team order (deterministic)

@@ -223,6 +223,35 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 }
 
 // store 8 float32 values as runtime out dtype (F32 / F16 / BF16) at element offset `elem`
+// ---- stores issued on every path
+// A store under a divergent branch leaves a path on which it was not issued. Loads and stores
+// retire in issue order on one counter, so where such paths join the compiler cannot count the
+// accesses issued after an earlier load, and the next use of that load waits for every access
+// in flight (the next row's loads and this row's stores included). A raw buffer store whose
+// offset lies at or past the resource's size is dropped by the hardware: a masked-off lane gets
+// such an offset and the store instruction itself is issued on every path.
+typedef __amdgpu_buffer_rsrc_t nf8_rsrc;
+constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every resource this library builds
+constexpr int kCpolNt = 2;                   // non-temporal
+__device__ __forceinline__ nf8_rsrc make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void st16_at(nf8_rsrc r, uint32_t off, uint4 v) {
+  const nf8_u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, kCpolNt);
+}
+// a strip read through a buffer resource at byte offset off: an offset at or past the
+// resource's size reads zeros (kOffNone: a zero strip)
+template <class T> __device__ __forceinline__ void load_strip_at(Strip<T> &s, nf8_rsrc r, uint32_t off) {
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(Strip<T>) / 16); ++i) {
+    const nf8_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * (uint32_t)i, 0, kCpolNt);
+    s.v[i] = make_uint4(v.x, v.y, v.z, v.w);
+  }
+}
+// 8 float32 values stored in the storage type T at byte offset off (kOffNone: nothing stored)
+template <class T> __device__ __forceinline__ void store_t8_at(nf8_rsrc r, uint32_t off, const float (&y)[8]);
+
 __device__ __forceinline__ void store_out8(void *base, int64_t elem, const float (&y)[8], int dt) {
   if (dt == DT_F32) {
     float *p = static_cast<float *>(base) + elem;
@@ -236,6 +265,17 @@ __device__ __forceinline__ void store_out8(void *base, int64_t elem, const float
     st_nt16(static_cast<uint16_t *>(base) + elem,
             make_uint4(pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]), pack_f16x2(y[4], y[5]),
                        pack_f16x2(y[6], y[7])));
+  }
+}
+
+template <class T> __device__ __forceinline__ void store_t8_at(nf8_rsrc r, uint32_t off, const float (&y)[8]) {
+  if constexpr (T::code == DT_F32) {
+    st16_at(r, off, make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])));
+    st16_at(r, off + 16u, make_uint4(__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7])));
+  } else if constexpr (T::code == DT_BF16) {
+    st16_at(r, off, make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])));
+  } else {
+    st16_at(r, off, make_uint4(pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]), pack_f16x2(y[4], y[5]), pack_f16x2(y[6], y[7])));
   }
 }
 

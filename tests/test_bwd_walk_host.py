@@ -1,11 +1,13 @@
 """Host replay of the backward row kernel's row walk at the planner's launch shapes (no GPU).
 
 The backward row kernel (``bwd_kernel`` in csrc/bwd.hip) runs a persistent grid of G
-workgroups, each of T teams. Workgroup b starts at base row b*T and advances by G*T, two rows
-per loop trip (two row buffers used in turn); team t handles row base + t. Its loads read a
-clamped row (row 0 past the end) and its dx stores are guarded by ``row < rows``. The planner's
-launch shape (layout, W, KC, T, G) comes from the library itself (``norm_bwd_launch_shape``), so
-this test follows the planner as built; the walk below restates the kernel's loop.
+workgroups, each of T teams. Workgroup b makes n = ceil((rows - b*T) / (G*T)) steps (none when
+b*T >= rows) at base rows b*T, b*T + G*T, ..., as n // 2 two-step trips (two row buffers used in
+turn) and a last single step when n is odd; team t handles row base + t. A team's row past the
+end reads zeros and its dx stores are dropped (their offset lies past the row's resource), the
+guard ``row < rows``. The planner's launch shape (layout, W, KC, T, G) comes from the library
+itself (``norm_bwd_launch_shape``), so this test follows the planner as built; the walk below
+restates the kernel's loop.
 
 [NVRTC-PR] "Migrate norms and softmax kernels to NVRTC", Flowchart: the backward's per-workgroup
 partial kernels and the grid sized from occupancy and the SM margin.
@@ -33,20 +35,30 @@ def launch_shape(rows, hidden, norm=L.NORM_LAYERNORM, with_add=0, cus=256, margi
 
 
 def walk(rows, T, G, teams=None, guarded=True):
-    """Rows the kernel stores dx for: workgroup b's loop visits base = b*T, b*T + G*T, ...
-    while base < rows (the loop's own test, and the break before the second step of a trip);
-    team t stores row base + t when it is < rows (``guarded``) or always (the unguarded form).
-    ``teams`` is the number of teams actually launched (T unless the kernel and the planner
-    disagree on T)."""
+    """Rows the kernel stores dx for: workgroup b makes n steps (the trip count computed from
+    its first base row b*T and the stride G*T), n // 2 trips of two steps and one more step
+    when n is odd, at base = b*T, b*T + G*T, ...; team t stores row base + t when it is < rows
+    (``guarded``) or always (the unguarded form). ``teams`` is the number of teams actually
+    launched (T unless the kernel and the planner disagree on T)."""
     teams = T if teams is None else teams
+    stride = G * T
     stored = []
+
+    def step(base):
+        for t in range(teams):
+            if not guarded or base + t < rows:
+                stored.append(base + t)
+
     for b in range(G):
-        base = b * T
-        while base < rows:
-            for t in range(teams):
-                if not guarded or base + t < rows:
-                    stored.append(base + t)
-            base += G * T
+        first = b * T
+        n = (rows - first + stride - 1) // stride if first < rows else 0
+        base = first
+        for _ in range(n // 2):
+            step(base)
+            step(base + stride)
+            base += 2 * stride
+        if n % 2:
+            step(base)
     return stored
 
 
