@@ -279,6 +279,13 @@ template <class T> __device__ __forceinline__ void store_t8_at(nf8_rsrc r, uint3
   }
 }
 
+// 8 float32 values stored in the output type dt at byte offset off (kOffNone: nothing stored)
+__device__ __forceinline__ void store_out8_at(nf8_rsrc r, uint32_t off, const float (&y)[8], int dt) {
+  if (dt == DT_F32) store_t8_at<F32>(r, off, y);
+  else if (dt == DT_BF16) store_t8_at<BF16>(r, off, y);
+  else store_t8_at<F16>(r, off, y);
+}
+
 // store 8 float32 values in the storage type T (used for dx)
 template <class T> __device__ __forceinline__ void store_t8(void *base, int64_t elem, const float (&y)[8]) {
   store_out8(base, elem, y, T::code);

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kSplitShapes[SH].threads) void fwd_split_kernel(Fwd
   }
   __syncthreads();
   const uint32_t tag = epoch_tag(s_epoch);
-  const int ticket = (int)s_ticket;
+  const int ticket = __builtin_amdgcn_readfirstlane((int)s_ticket);  // (scalar: so are the row and slice indices)
   const int group = ticket / S;
   const int slice = ticket - group * S;
   const int ngroups = (int)gridDim.x / S;
@@ -249,6 +249,11 @@ __global__ __launch_bounds__(kSplitShapes[SH].threads) void fwd_split_kernel(Fwd
         if (p.mu) p.mu[r] = mu;
       }
     }
+    // (the row's y stores are issued on every path: buffer stores whose offset is moved past
+    // the slice's end where a lane has nothing to write; a path on which a strip's store was
+    // skipped would make the next wait for an earlier load drain every access in flight)
+    const uint32_t ob = p.out_dtype == DT_F32 ? 4u : 2u;
+    const nf8_rsrc ry = make_rsrc(static_cast<char *>(p.y) + (r * H + c0) * ob, (uint32_t)cols * ob);
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       const int c = 8 * (tid + NT * k);
@@ -273,7 +278,7 @@ __global__ __launch_bounds__(kSplitShapes[SH].threads) void fwd_split_kernel(Fwd
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = (xv[i] * rs) * gk[i];
       }
-      if (cv[k]) store_out8(p.y, r * H + c0 + c, y, p.out_dtype);
+      store_out8_at(ry, cv[k] ? (uint32_t)c * ob : kOffNone, y, p.out_dtype);
       __builtin_amdgcn_sched_barrier(0);  // one strip's weights and values live at a time
     }
   };
