@@ -277,7 +277,8 @@ int norm_bwd_launch_shape(int64_t rows, int64_t hidden, int in_dtype, int w_dtyp
  * occupancy grid), NORMFP8_BAND_CLASSES (1: one ticket class), NORMFP8_SPLIT (0: no split
  * kernel for long rows; 1: split kernel for every row it covers), NORMFP8_COLX (0: two-pass
  * routes instead of the single-pass columnwise kernel), NORMFP8_SPLIT_SHAPE (0: the 16-wave
- * split shape, 16384-column slices; 1: the 8-wave shape, 32768-column slices, 16-bit input).
+ * split shape, 16384-column slices; 1 / 2: the 8-wave shapes with 32768- / 16384-column slices,
+ * 16-bit input).
  * Unknown names give
  * NORM_ERR_INVALID_ARG. Not for the hot path of an application: a change affects every later
  * call in the process.

@@ -183,11 +183,16 @@ struct FwdPlan {
 // the band kernel); up to 65536 the one-workgroup-per-row layout is faster (LayerNorm
 // 1024 x 65536: 68 against 72 us; RMSNorm 52 against 63 us)
 constexpr int64_t kSplitMinHidden = 65536 + 8;
-// LayerNorm with a 16-bit input: the 8-wave split shape (gamma in registers, beta in LDS) from
-// rows of 40961 elements on (bf16, one box: 1536 x 49152 78 against 81-85 us in the row layout,
-// 1024 x 65536 65 against 67-74, 682 x 98304 67 against 77 for the 16-wave shape, 512 x 131072
-// 69 against 85)
-constexpr int64_t kSplitMinHiddenLn16 = 40960 + 1;
+// 16-bit input, the 8-wave shapes with gamma in registers (bf16, one box, against the default
+// before them): LayerNorm from 32769 elements, 16384-column slices up to 49152 (2048 x 40960
+// 84.6 against 96.3 us in the row layout, 1536 x 49152 69.2 against 73.8 on 32768-column
+// slices, whose second slice would hold 16384 columns) and 32768-column slices beyond (1024 x
+// 57344 58.5 against 63.5 on 16384 columns); RMSNorm from 65537, 16384-column slices up to
+// 131072 (768 x 81920 54.8 against 59.8 us, 512 x 131072 57.6 against 62.3 on the 16-wave
+// shape) and 32768-column slices beyond (256 x 262144 65.6 against 114.6 in the band kernel)
+constexpr int64_t kSplitMinHiddenLn16 = 32768 + 1;
+constexpr int64_t kSplitShape2MaxLn16 = 49152;
+constexpr int64_t kSplitShape2MaxRms16 = 131072;
 
 int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dtype, int norm_type,
              int scaling, int qlayout, int cu_margin, FwdPlan *pl) {
@@ -325,18 +330,20 @@ int plan_fwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int out_dt
   }
 
   // long rows without an FP8 epilogue: the split kernel (NORMFP8_SPLIT=0 keeps the row / band
-  // layouts, =1 takes the split kernel for any row it covers; NORMFP8_SPLIT_SHAPE=0 / 1 picks its
-  // shape)
+  // layouts, =1 takes the split kernel for any row it covers; NORMFP8_SPLIT_SHAPE=0 / 1 / 2 picks
+  // its shape)
   {
     const int force = knob(K_SPLIT, -1);
-    // shape 1 (8 waves x 8 strips, gamma in registers) takes 16-bit input only; by default it
-    // serves LayerNorm, RMSNorm keeps the 16-wave shape (its weights fit LDS whole)
+    // shapes 1 and 2 (8 waves, gamma in registers) take 16-bit input only: the shape whose slices
+    // divide the row more evenly (a short last slice idles its workgroups for most of a row)
     const bool in16 = in_dtype != DT_F32;
+    const bool ln = norm_type == NORM_LAYERNORM;
     const int shape_ov = knob(K_SPLIT_SHAPE, -1);
-    int shape = norm_type == NORM_LAYERNORM && in16 ? 1 : 0;
+    int shape = 0;
+    if (in16) shape = hidden <= (ln ? kSplitShape2MaxLn16 : kSplitShape2MaxRms16) ? 2 : 1;
     if (shape_ov == 0) shape = 0;
-    else if (shape_ov == 1 && in16) shape = 1;
-    const int64_t min_hidden = shape == 1 ? kSplitMinHiddenLn16 : kSplitMinHidden;
+    else if ((shape_ov == 1 || shape_ov == 2) && in16) shape = shape_ov;
+    const int64_t min_hidden = in16 && ln ? kSplitMinHiddenLn16 : kSplitMinHidden;
     const int64_t S = cdiv(hidden, kSplitShapes[shape].cols());
     const bool fits = pl->mode == MODE_PLAIN && !pl->colwise && !pl->gen && !force_band && S <= kSplitMaxSlices;
     if (fits && (force == 1 || (force < 0 && hidden >= min_hidden))) {

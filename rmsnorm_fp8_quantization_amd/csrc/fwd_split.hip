@@ -11,12 +11,13 @@
 // of its row group and loads the slice's gamma / beta (float32, 1 + gamma when zero-centred)
 // once, then walks its rows, so no weight is read again from the caches per row (a 65536-element
 // row re-read 512 KB of weights per row through the L2 in the one-workgroup-per-row layout).
-// Lane t holds the strips of columns 8 (t + NT k), k < KC. Two shapes: 16 waves x 2 strips
+// Lane t holds the strips of columns 8 (t + NT k), k < KC. Three shapes: 16 waves x 2 strips
 // (W = 16384) with both weight arrays in LDS (128 KB for LayerNorm) and four rows in flight; and,
 // for 16-bit input, 8 waves x 8 strips (W = 32768) with gamma in registers (64 per lane), beta in
-// LDS (128 KB) and three rows in flight.
+// LDS (128 KB) and three rows in flight, or 8 waves x 4 strips (W = 16384) with gamma in
+// registers (32 per lane), beta in LDS (64 KB) and four rows in flight.
 //
-// Per row: every wave reduces its elements of the slice (1024 or 4096; LayerNorm: deviations
+// Per row: every wave reduces its elements of the slice (1024, 2048 or 4096; LayerNorm: deviations
 // from the wave's plain mean estimate, so that a large common part of the row costs no
 // precision), the waves' partials are merged through LDS in wave order, and the slice's partial is published to the
 // workspace as tagged 64-bit words {value, launch tag}. Each workgroup then polls the S slices'
@@ -24,8 +25,8 @@
 // statistics. Four rows are in flight: row j + 3 is loading and row j + 2 publishes its partial
 // while row j is normalised with its partners' words, which were published two rows earlier and
 // loaded one row earlier, so the exchange overlaps the loads of the next rows. With three rows
-// in flight (the 8-wave shape, whose registers hold gamma) row j + 2 loads and row j + 1
-// publishes while row j is normalised: each stage has one row's time to land.
+// in flight (the 32768-column shape, whose registers hold 64 gamma values) row j + 2 loads and
+// row j + 1 publishes while row j is normalised: each stage has one row's time to land.
 //
 // Group membership comes from tickets taken at start (group = ticket / S, slice = ticket % S):
 // every ticket is held by a running workgroup, so a workgroup only waits on workgroups that are
@@ -345,10 +346,10 @@ __global__ __launch_bounds__(kSplitShapes[SH].threads) void fwd_split_kernel(Fwd
 
 template <int NORM>
 static const void *pick_split_in(int in_dtype, int shape) {
-  if (shape == 1) {  // (16-bit input only: three float32 rows would not fit beside gamma)
+  if (shape == 1 || shape == 2) {  // (16-bit input only: float32 rows would not fit beside gamma)
     switch (in_dtype) {
-      case DT_BF16: return (const void *)fwd_split_kernel<NORM, BF16, 1>;
-      case DT_F16: return (const void *)fwd_split_kernel<NORM, F16, 1>;
+      case DT_BF16: return shape == 1 ? (const void *)fwd_split_kernel<NORM, BF16, 1> : (const void *)fwd_split_kernel<NORM, BF16, 2>;
+      case DT_F16: return shape == 1 ? (const void *)fwd_split_kernel<NORM, F16, 1> : (const void *)fwd_split_kernel<NORM, F16, 2>;
       default: return nullptr;
     }
   }

@@ -81,13 +81,15 @@ constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1, 4}, {4, 1, 2}, {4, 2, 2}, {8, 
 // ---- forward split kernel: S workgroups per row, each holding one slice of every row of its row
 // group. Shape 0 (any input dtype): 16 waves x 2 strips, a 16384-column slice, its weights in
 // LDS, four rows in flight. Shape 1 (16-bit input): 8 waves x 8 strips, a 32768-column slice,
-// gamma in registers and beta (LayerNorm) in LDS, three rows in flight.
+// gamma in registers and beta (LayerNorm) in LDS, three rows in flight. Shape 2 (16-bit input):
+// 8 waves x 4 strips, a 16384-column slice, gamma in registers and beta in LDS, four rows in
+// flight.
 struct SplitShape {
   int threads, strips, wreg, depth;
   constexpr int64_t cols() const { return 8LL * threads * strips; }
 };
-constexpr SplitShape kSplitShapes[2] = {{1024, 2, 0, 4}, {512, 8, 1, 3}};
-constexpr int kSplitMaxSlices = 8;  // shape 0: rows up to 131072 elements; shape 1: 262144
+constexpr SplitShape kSplitShapes[3] = {{1024, 2, 0, 4}, {512, 8, 1, 3}, {512, 4, 1, 4}};
+constexpr int kSplitMaxSlices = 8;  // shapes 0 and 2: rows up to 131072 elements; shape 1: 262144
 
 // ---- single-pass columnwise kernel: 8 waves, 128-row bands of 512-column slices
 constexpr int kColxThreads = 512;

@@ -62,11 +62,11 @@ PLAIN_CASES = [
     # LayerNorm 16385..32768, 16-bit input: 8 waves with the weights in registers
     (LN, BF16, 16392, W8_K8), (LN, BF16, 20480, W8_K8), (LN, F16, 32768, W8_K8),
     (LN, F32, 20480, W16_K4),
-    (LN, BF16, 32776, W16_K8), (LN, BF16, 40960, W16_K8),
+    (LN, F32, 32776, W16_K8), (LN, F32, 40960, W16_K8),
     (RMS, BF16, 256, W1_K1), (RMS, BF16, 4096, W2T2_K4), (RMS, BF16, 8192, W4_K4),
     (RMS, BF16, 12288, W16_K2), (RMS, BF16, 16384, W16_K2),
-    (RMS, BF16, 20480, W16_K4), (RMS, F32, 32768, W16_K4), (RMS, BF16, 65536, W16_K8),
-    (LN, F32, 65536, W16_K8),
+    (RMS, BF16, 20480, W16_K4), (RMS, F32, 32768, W16_K4), (RMS, BF16, 40960, W16_K8),
+    (RMS, BF16, 65536, W16_K8), (LN, F32, 65536, W16_K8),
 ]
 
 
@@ -135,24 +135,28 @@ def test_single_pass_columnwise_conditions():
 
 
 @pytest.mark.parametrize("norm,in_dt,hidden,shape,S", [
-    # LayerNorm, 16-bit input, beyond 40960: 8 waves x 8 strips with gamma in registers
-    (LN, BF16, 40968, 1, 2), (LN, BF16, 49152, 1, 2), (LN, BF16, 65536, 1, 2), (LN, F16, 65544, 1, 3),
-    (LN, BF16, 262144, 1, 8),
-    # float32 input or RMSNorm: 16 waves x 2 strips with the weights in LDS, beyond 65536
-    (LN, F32, 65544, 0, 5), (LN, F32, 98304, 0, 6), (RMS, BF16, 65544, 0, 5), (RMS, F32, 131072, 0, 8),
+    # LayerNorm, 16-bit input: 8 waves with gamma in registers, 16384-column slices from 32769 to
+    # 49152 elements, 32768-column slices beyond
+    (LN, BF16, 32776, 2, 3), (LN, BF16, 40960, 2, 3), (LN, F16, 49152, 2, 3),
+    (LN, BF16, 49160, 1, 2), (LN, BF16, 65536, 1, 2), (LN, F16, 65544, 1, 3), (LN, BF16, 262144, 1, 8),
+    # RMSNorm, 16-bit input: the same shapes from 65537, 16384-column slices up to 131072
+    (RMS, BF16, 65544, 2, 5), (RMS, F16, 131072, 2, 8), (RMS, BF16, 131080, 1, 5), (RMS, BF16, 262144, 1, 8),
+    # float32 input: 16 waves x 2 strips with the weights in LDS, beyond 65536
+    (LN, F32, 65544, 0, 5), (LN, F32, 98304, 0, 6), (RMS, F32, 131072, 0, 8),
 ])
 def test_long_rows_take_the_split_kernel(norm, in_dt, hidden, shape, S):
     s = plan(1000, hidden, norm, in_dt)
     assert s == (L.NORM_ROUTE_SPLIT, shape, 0, 0, 0, S)
-    cols = 16384 if shape == 0 else 32768  # columns one workgroup's slice holds
+    cols = 32768 if shape == 1 else 16384  # columns one workgroup's slice holds
     assert (S - 1) * cols < hidden <= S * cols
 
 
 def test_split_threshold_edges():
-    assert plan(1000, 40960, LN)[0] == L.NORM_ROUTE_ROW
-    assert plan(1000, 40968, LN)[0] == L.NORM_ROUTE_SPLIT
+    assert plan(1000, 32768, LN)[0] == L.NORM_ROUTE_ROW
+    assert plan(1000, 32776, LN)[0] == L.NORM_ROUTE_SPLIT
     assert plan(1000, 65536, LN, F32)[0] == L.NORM_ROUTE_ROW
     assert plan(1000, 65536, RMS)[0] == L.NORM_ROUTE_ROW
+    assert plan(1000, 65544, RMS)[0] == L.NORM_ROUTE_SPLIT
     # an FP8 epilogue never takes the split kernel
     assert plan(1000, 49152, LN, scaling=DELAYED)[0] == L.NORM_ROUTE_ROW
 
@@ -161,6 +165,8 @@ def test_band_kernel_beyond_the_row_and_split_layouts():
     # plain rows beyond what 8 split slices hold: band tiles of 8 rows x 4096 columns
     s = plan(200, 200000, LN, F32)
     assert s == (L.NORM_ROUTE_BAND, 4, 0, 0, 0, 49)
+    # beyond eight 32768-column slices and 64 band slices of 4096 columns: the general kernels
+    assert plan(200, 262152, RMS) == (L.NORM_ROUTE_GENERAL, 0, 0, 0, 0, 1)
     # an FP8 rowwise epilogue beyond 65536 (no row layout covers it, no split for FP8)
     s = plan(200, 100000, RMS, scaling=DELAYED)
     assert s == (L.NORM_ROUTE_BAND, 4, 0, 0, 0, 25)

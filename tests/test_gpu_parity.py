@@ -152,7 +152,8 @@ def test_fwd_layernorm_8k_to_32k_register_weights(in_dt, out_dt, rows, hidden):
                                             ("rmsnorm", 12288, True), ("rmsnorm", 10232, False),
                                             ("rmsnorm", 16384, False), ("layernorm", 12288, True),
                                             ("layernorm", 10232, False), ("rmsnorm", 4096, True),
-                                            ("rmsnorm", 2056, False)])
+                                            ("rmsnorm", 2056, False), ("layernorm", 45056, False),
+                                            ("rmsnorm", 98304, False), ("rmsnorm", 196608, True)])
 def test_fwd_long_rows(w_dt, mode, norm, hidden, zc):
     rows = 5
     case = workloads.small_case(norm, rows, hidden, "bf16", w_dt, seed=hidden % 97 + rows, zero_centered_gamma=zc)
@@ -646,19 +647,20 @@ def test_fwd_then_bwd_end_to_end():
 # ------------------------------------------------------------------------------ split rows
 
 SPLIT_SHAPES = [(3, 8), (5, 4096), (37, 16384), (9, 16392), (300, 40000), (2, 65536), (70, 65536),
-                (4, 131072), (1, 98304), (520, 65536)]
+                (4, 131072), (1, 98304), (520, 65536), (3, 196608), (2, 262144)]
 
 
-@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("shape", [0, 1, 2])
 @pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
 @pytest.mark.parametrize("in_dt", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("rows,hidden", SPLIT_SHAPES)
 def test_fwd_split_rows(norm, in_dt, rows, hidden, shape):
     """The split kernel (S = ceil(hidden / W) workgroups per row, tagged partial exchange),
     forced on every shape: one to eight slices, ragged last slices, fewer rows than row groups
-    and several rows per group. Shape 0: 16384-column slices with the weights in LDS, four rows
-    in flight; shape 1 (16-bit input; float32 input stays on shape 0): 32768-column slices with
-    gamma in registers and beta in LDS, three rows in flight."""
+    and several rows per group (rows needing more than eight slices of the forced shape go to
+    the band or general kernels). Shape 0: 16384-column slices with the weights in LDS, four rows
+    in flight; shapes 1 and 2 (16-bit input; float32 input stays on shape 0): 32768- or
+    16384-column slices with gamma in registers and beta in LDS, three or four rows in flight."""
     case = workloads.small_case(norm, rows, hidden, in_dt, "f32", seed=rows + hidden + 11)
     ref = oracle_fwd(case, norm, in_dt, "f32", False)
     x, g, b = gpu(case, "x", "gamma", "beta")
@@ -671,7 +673,7 @@ def test_fwd_split_rows(norm, in_dt, rows, hidden, shape):
     assert_ws_clean()
 
 
-@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("shape", [0, 1, 2])
 @pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
 def test_fwd_split_zero_centered_bf16_weights_and_margin(norm, shape):
     rows, hidden = 33, 49152
@@ -834,12 +836,14 @@ def test_repeat_runs_are_bitwise_identical():
             fs = nf.fwd(x, g, b, norm="layernorm")                 # split kernel (two slices)
         with env(NORMFP8_SPLIT=1, NORMFP8_SPLIT_SHAPE=1):
             fs1 = nf.fwd(xw, gw, bw, norm="layernorm")             # 8-wave split shape (two slices)
+        with env(NORMFP8_SPLIT=1, NORMFP8_SPLIT_SHAPE=2):
+            fs2 = nf.fwd(xw, gw, bw, norm="layernorm")             # 16384-column 8-wave shape (three slices)
         with env(NORMFP8_COL_KERNEL=0):
             fb = nf.fwd(x, g, b, norm="layernorm", scaling="mxfp8", layout="rowwise_colwise")
         fc = nf.fwd(x, g, b, norm="layernorm", scaling="mxfp8", layout="rowwise_colwise")
         d = nf.bwd(dys, xs, f["mu"], f["rsigma"], gs, norm="layernorm")
         outs.append([t.clone() for t in (f["y"], f["mu"], f["rsigma"], fs["y"], fs["mu"], fs["rsigma"],
-                                          fs1["y"], fs1["mu"], fs1["rsigma"],
+                                          fs1["y"], fs1["mu"], fs1["rsigma"], fs2["y"], fs2["mu"], fs2["rsigma"],
                                           fb["y"], fb["y_colwise"], fb["rsigma"],
                                           fc["y"], fc["y_colwise"], fc["colwise_scale_inv"],
                                           d["dx"], d["dgamma"], d["dbeta"], *outs_x)])
