@@ -427,7 +427,7 @@ int plan_bwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_t
   if (ov >= 0 && ov < BWD_NCFG && kBwdShapes[ov].cover() >= hidden) {
     cfg = ov;
   } else {
-    const int pref[] = {BWD_W2_K1, BWD_W4_K1, BWD_W4_K2, BWD_W8_K2, BWD_W8_K3, BWD_W16_K2};
+    const int pref[] = {BWD_W2_K1, BWD_W4_K1, BWD_W4_K2, BWD_W5_K2_T2, BWD_W8_K2, BWD_W8_K3, BWD_W16_K2};
     for (int c : pref)
       if (kBwdShapes[c].cover() >= hidden) {
         cfg = c;
@@ -448,6 +448,7 @@ int plan_bwd(int64_t rows, int64_t hidden, int in_dtype, int w_dtype, int norm_t
     if (cfg == BWD_W2_K1) cfg = BWD_W2_K1_T1;
     else if (cfg == BWD_W4_K1) cfg = BWD_W4_K1_T1;
     else if (cfg == BWD_W4_K2) cfg = BWD_W4_K2_T1;
+    else if (cfg == BWD_W5_K2_T2) cfg = BWD_W5_K2_T1;
   }
   pl->cfg = cfg;
   const int64_t gmax = (int64_t)kMaxCus * bwd_wgs_per_cu(cfg);

@@ -327,6 +327,8 @@ static const void *pick_bwd_cfg(int cfg) {
     case BWD_W4_K1_T1: return NF8_BWD(BWD_W4_K1_T1);
     case BWD_W4_K2_T1: return NF8_BWD(BWD_W4_K2_T1);
     case BWD_W8_K3: return NF8_BWD(BWD_W8_K3);
+    case BWD_W5_K2_T2: return NF8_BWD(BWD_W5_K2_T2);
+    case BWD_W5_K2_T1: return NF8_BWD(BWD_W5_K2_T1);
     default: return nullptr;
   }
 #undef NF8_BWD

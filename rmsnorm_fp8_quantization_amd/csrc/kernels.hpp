@@ -63,6 +63,8 @@ enum BwdCfg : int {
   BWD_W4_K1_T1,
   BWD_W4_K2_T1,
   BWD_W8_K3,     // 8 waves x 3 strips: rows up to 12288 with the next row in flight
+  BWD_W5_K2_T2,  // 5 waves x 2 strips, two teams: an exact cover of 5120-element rows
+  BWD_W5_K2_T1,  // its one-team twin
   BWD_NCFG
 };
 // T teams of W waves per workgroup, each team on its own row; the teams share one partial
@@ -76,7 +78,8 @@ struct BwdShape {
 // and the kernels must agree on every team count, thread count and tile size)
 constexpr BwdShape kBwdShapes[BWD_NCFG] = {{2, 1, 4}, {4, 1, 2}, {4, 2, 2}, {8, 2, 1},
                                            {16, 2, 1}, {8, 1, 1}, {16, 1, 1}, {4, 4, 1},
-                                           {2, 1, 1}, {4, 1, 1}, {4, 2, 1}, {8, 3, 1}};
+                                           {2, 1, 1}, {4, 1, 1}, {4, 2, 1}, {8, 3, 1},
+                                           {5, 2, 2}, {5, 2, 1}};
 
 // ---- forward split kernel: S workgroups per row, each holding one slice of every row of its row
 // group. Shape 0 (any input dtype): 16 waves x 2 strips, a 16384-column slice, its weights in

@@ -62,7 +62,7 @@ def walk(rows, T, G, teams=None, guarded=True):
     return stored
 
 
-LAYOUTS = range(12)  # every backward layout of the library's shape table
+LAYOUTS = range(14)  # every backward layout of the library's shape table
 
 
 @pytest.mark.parametrize("cfg", LAYOUTS)
@@ -119,3 +119,22 @@ def test_kernel_and_planner_disagreeing_on_t_store_past_the_end():
     assert max(bad) == 16384
     ok = walk(16384, 3, G, teams=2, guarded=True)
     assert max(ok) < 16384 and len(set(ok)) < 16384
+
+
+# default backward layout per row width (many rows: 16384; few rows: under four per team)
+@pytest.mark.parametrize("hidden,many,few", [
+    (1024, (0, 2, 1, 4), (8, 2, 1, 1)),
+    (2048, (1, 4, 1, 2), (9, 4, 1, 1)),
+    (4096, (2, 4, 2, 2), (10, 4, 2, 1)),
+    (4104, (12, 5, 2, 2), (13, 5, 2, 1)),
+    (5120, (12, 5, 2, 2), (13, 5, 2, 1)),
+    (5128, (3, 8, 2, 1), (3, 8, 2, 1)),
+    (8192, (3, 8, 2, 1), (3, 8, 2, 1)),
+    (12288, (11, 8, 3, 1), (11, 8, 3, 1)),
+    (16384, (4, 16, 2, 1), (4, 16, 2, 1)),
+])
+def test_default_layout_per_width(hidden, many, few):
+    assert launch_shape(16384, hidden)[:4] == many
+    assert launch_shape(16384, hidden, norm=L.NORM_RMSNORM)[:4] == many
+    assert launch_shape(256 * many[3] * 4 - 1, hidden)[:4] == few
+    assert launch_shape(256 * many[3] * 4, hidden)[:4] == many

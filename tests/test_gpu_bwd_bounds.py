@@ -42,7 +42,7 @@ def _team_count(rows, hidden, norm_code, add):
     return int(shape[3])
 
 
-@pytest.mark.parametrize("rows,hidden", [(2049, 4096), (4097, 1024), (2049, 2048), (4099, 512)])
+@pytest.mark.parametrize("rows,hidden", [(2049, 4096), (4097, 1024), (2049, 2048), (4099, 512), (2049, 5120)])
 @pytest.mark.parametrize("kind", ["layernorm", "rmsnorm", "rmsnorm_add"])
 def test_multi_team_backward_stays_inside_dx(rows, hidden, kind):
     norm = "layernorm" if kind == "layernorm" else "rmsnorm"

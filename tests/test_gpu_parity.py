@@ -101,7 +101,7 @@ def test_fwd_plain_other_out_dtype_and_bf16_weights(out_dt):
 
 ROW_COVER = [512, 1024, 2048, 4096, 4096, 8192, 16384, 4096, 4096, 4096, 65536, 8192, 16384, 16384,
              32768, 32768, 16384]   # per row layout
-BWD_COVER = [1024, 2048, 4096, 8192, 16384, 4096, 8192, 8192, 1024, 2048, 4096, 12288]
+BWD_COVER = [1024, 2048, 4096, 8192, 16384, 4096, 8192, 8192, 1024, 2048, 4096, 12288, 5120, 5120]
 
 
 @pytest.mark.parametrize("cfg", range(len(ROW_COVER)))
