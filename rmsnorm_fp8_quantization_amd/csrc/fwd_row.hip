@@ -300,15 +300,15 @@ __global__ __launch_bounds__(64 * P * T) void fwd_row_kernel(FwdRowParams p) {
     // weights live at a time)
 #pragma unroll
     for (int k = 0; k < (MODE == MODE_STATS ? 0 : KC); ++k) {
-      // delayed scaling, four or more strips per lane: a strip that lies past the row's end for
-      // the whole team is skipped (no weights, arithmetic or store). The test is the same for
-      // every lane of the team, so its waves stay balanced; skipping per lane, where only some
-      // waves of a team are past the end, gained nothing. The branch itself costs a few percent
-      // where it never skips, so layouts of fewer strips, which rarely have a whole strip past
-      // the end, go without it, and so does plain output, which measured the same either way.
-      // (WL == 2 loads later strips' weights in this pass; MXFP8 reduces over the four lanes
-      // of a block.)
-      if constexpr (WL != 2 && MODE == MODE_DELAYED && KC >= 4) {
+      // FP8 output, four or more strips per lane: a strip that lies past the row's end for the
+      // whole team is skipped (no weights, arithmetic or store; with MXFP8 no lane of any of its
+      // blocks is inside the row). The test is the same for every lane of the team, so its
+      // waves stay balanced; skipping per lane, where only some waves of a team are past the
+      // end, gained nothing. The branch itself costs a few percent where it never skips, so
+      // layouts of fewer strips, which rarely have a whole strip past the end, go without it,
+      // and so does plain output, which measured the same either way. (WL == 2 loads later
+      // strips' weights in this pass.)
+      if constexpr (WL != 2 && (MODE == MODE_DELAYED || MODE == MODE_MX) && KC >= 4) {
         if (8 * (int64_t)TEAM * k >= H) continue;
       }
       const bool ok = rv && cv[k];
