@@ -125,6 +125,20 @@ def check_fp8(codes_g: np.ndarray, codes_ref: np.ndarray, u_exact: np.ndarray, f
     # +0 / -0 are the same value
     zero_pair = (F.fp8_decode(cg[diff], fmt) == 0) & (F.fp8_decode(cr[diff], fmt) == 0)
     far = ~((dist[diff] <= 1) | zero_pair)
+    # LayerNorm (`slack` given): a value near zero is the binary32 sum of terms that cancel, and
+    # where the code spacing is finer than that evaluation allowance (E5M2 near zero) the code
+    # can be several steps off. Such a code passes when its value lies within the allowance plus
+    # one code spacing of the exact scaled value; it counts against the same allowance budget.
+    multi = np.zeros_like(far)
+    if far.any() and slack is not None:
+        vgf = F.fp8_decode(cg[diff][far], fmt)
+        uf = np.clip(np.asarray(u_exact, np.float64)[diff][far], -fmt.max_finite, fmt.max_finite)
+        ef = np.floor(np.log2(np.maximum(np.abs(vgf), 2.0 ** fmt.emin)))
+        spacing = 2.0 ** (np.maximum(ef, fmt.emin) - fmt.mant_bits)
+        within = np.abs(vgf - uf) <= np.asarray(slack, np.float64)[diff][far] + spacing
+        fi = np.flatnonzero(far)
+        multi[fi[within]] = True
+        far[fi[within]] = False
     if far.any():
         idx = np.argwhere(diff)[far][:6]
         raise AssertionError(
@@ -139,7 +153,7 @@ def check_fp8(codes_g: np.ndarray, codes_ref: np.ndarray, u_exact: np.ndarray, f
     strict_ok = (np.abs(u - mid) <= bound) | zero_pair
     if slack is not None:
         bound = bound + np.asarray(slack, np.float64)[diff]
-    ok = (np.abs(u - mid) <= bound) | zero_pair
+    ok = (np.abs(u - mid) <= bound) | zero_pair | multi
     n_slack = int((ok & ~strict_ok).sum())  # on a boundary only within the LayerNorm allowance
     if not np.all(ok):
         bad = ~ok

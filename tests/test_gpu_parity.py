@@ -212,7 +212,8 @@ def test_fwd_zero_centered_gamma_and_zero_rows():
 @pytest.mark.parametrize("layout", ["rowwise", "rowwise_colwise", "colwise"])
 @pytest.mark.parametrize("norm,rows,hidden", [("rmsnorm", 64, 1024), ("rmsnorm", 45, 4104),
                                               ("layernorm", 100, 2048), ("rmsnorm", 33, 20480),
-                                              ("layernorm", 50, 4096), ("rmsnorm", 130, 3072)])
+                                              ("layernorm", 50, 4096), ("rmsnorm", 130, 3072),
+                                              ("layernorm", 40, 5120), ("layernorm", 24, 10240)])
 def test_fwd_delayed(fp8, layout, norm, rows, hidden):
     case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=rows)
     xh = case["x"].float()
@@ -289,7 +290,8 @@ def test_fwd_delayed_amax_inplace_and_accumulates():
 @pytest.mark.parametrize("layout", ["rowwise", "rowwise_colwise", "colwise"])
 @pytest.mark.parametrize("norm,rows,hidden,zc", [("rmsnorm", 64, 1024, True), ("rmsnorm", 45, 1000, False),
                                                  ("layernorm", 96, 4096, False), ("rmsnorm", 32, 12288, True),
-                                                 ("rmsnorm", 7, 512, False)])
+                                                 ("rmsnorm", 7, 512, False), ("layernorm", 40, 6144, False),
+                                                 ("layernorm", 24, 10240, True)])
 def test_fwd_mxfp8(fp8, layout, norm, rows, hidden, zc):
     case = workloads.small_case(norm, rows, hidden, "bf16", "f32", seed=hidden + rows, zero_centered_gamma=zc)
     ref = oracle_fwd(case, norm, "bf16", "f32", zc)
